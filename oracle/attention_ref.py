@@ -1,0 +1,168 @@
+"""Plain fp64 CPU oracle for exact (softmax) attention: forward, backward, decode.
+
+TEST INFRASTRUCTURE. This module is the checker, not the product: only the
+tests, the package smoke check and the benchmark's CPU-baseline leg import it.
+It shares no code with the HIP library and imports nothing from the package.
+
+What it computes is the plain three-step definition (scores, probabilities,
+weighted values), never the tiled online recurrence:
+  * zerotofrontier "Efficient attention: memory-bound", section "Standard
+    attention, kernel by kernel": S from Q and K, P as the row softmax of S,
+    O = P V, with the scores scaled by 1/sqrt(d_k) (section "Real code moves
+    even more" names the scale step);
+  * same page, section "The obstacle, a normalizer that needs the whole row":
+    P_ij uses the row maximum m_i only for safety and the normaliser l_i;
+  * kgptalkie "Flash Attention: Why Memory Traffic, Not Compute, Is the
+    Bottleneck", section "Causal Masks Still Apply": a query sees keys up to
+    and including its own position;
+  * aimlrounds "FlashAttention", section "Softmax without seeing the whole
+    row": the per-row log-sum-exp kept for the backward pass;
+  * zerotofrontier page, section "Real code moves even more": the backward
+    products dV = P^T dO, dP = dO V^T, dS from P and dP, dQ and dK from dS.
+
+Readings taken where the pages are silent (each is pinned by a test):
+  * causal with Tq != Tk aligns the diagonal bottom-right: key j is visible to
+    query i iff j <= i + (Tk - Tq);
+  * a query with no visible key (only causal with Tq > Tk) has O = 0 and
+    LSE = -inf, and contributes nothing to any gradient;
+  * LSE is the natural log of sum_j exp(S_ij), S already scaled;
+  * the softmax backward is the textbook Jacobian:
+    dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik);
+  * grouped KV heads are contiguous groups: query head h uses KV head
+    h // (Hq // Hkv); dK and dV sum over the group.
+
+Rows are independent, so every function may work on any subset of query rows
+(the full-size checks evaluate sampled rows one block at a time). Keys are
+never split: each row always sees its whole score row at once.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_ROW_BLOCK = 512
+
+
+def visible(rows: np.ndarray, Tq: int, Tk: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), Tk]: may query row i look at key j."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if not causal:
+        return np.ones((rows.shape[0], Tk), dtype=bool)
+    j = np.arange(Tk, dtype=np.int64)
+    return j[None, :] <= rows[:, None] + (Tk - Tq)
+
+
+def row_probs(q_rows: np.ndarray, k: np.ndarray, scale: float, rows: np.ndarray,
+              Tq: int, causal: bool):
+    """Scores, probabilities and log-sum-exp for some query rows of one head.
+
+    q_rows [n,d], k [Tk,d] (fp64). Returns P [n,Tk] (zero where masked and for
+    empty rows) and lse [n] (-inf for empty rows)."""
+    Tk = k.shape[0]
+    s = scale * (q_rows @ k.T)
+    vis = visible(rows, Tq, Tk, causal)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.where(vis, np.exp(s - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    p = e / l_safe[:, None]
+    lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    return p, lse
+
+
+def _kv_head(hq: int, Hq: int, Hkv: int) -> int:
+    return hq // (Hq // Hkv)
+
+
+def attention_fwd(q, k, v, scale: float, causal: bool, rows=None):
+    """Forward: O [B,Hq,n,d] and LSE [B,Hq,n] for query rows `rows` (all if None).
+
+    q [B,Hq,Tq,d]; k, v [B,Hkv,Tk,d]; any float dtype, computed in fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    assert Hq % Hkv == 0 and k.shape[0] == B and v.shape == k.shape
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, Hq, rows.shape[0], v.shape[3]))
+    lse = np.zeros((B, Hq, rows.shape[0]))
+    for b in range(B):
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            for s in range(0, rows.shape[0], _ROW_BLOCK):
+                r = rows[s:s + _ROW_BLOCK]
+                p, l = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal)
+                o[b, h, s:s + _ROW_BLOCK] = p @ v[b, hk]
+                lse[b, h, s:s + _ROW_BLOCK] = l
+    return o, lse
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool):
+    """Backward of O = softmax(scale Q K^T [+mask]) V given dO.
+
+    Returns dQ [B,Hq,Tq,d], dK and dV [B,Hkv,Tk,d] in fp64. P is recomputed
+    here from Q and K (this oracle never sees the GPU's O or LSE)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            for s in range(0, Tq, _ROW_BLOCK):
+                r = np.arange(s, min(Tq, s + _ROW_BLOCK))
+                p, _ = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal)
+                g = do[b, h, r]
+                dv[b, hk] += p.T @ g
+                dp = g @ v[b, hk].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h, r] = scale * (ds @ k[b, hk])
+                dk[b, hk] += scale * (ds.T @ q[b, h, r])
+    return dq, dk, dv
+
+
+def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows):
+    """dQ for some query rows of one (batch, query head): each row's gradient
+    needs only that row's own scores, so it can be evaluated at any size."""
+    q = np.asarray(q[b, h], dtype=np.float64)
+    Hq, Hkv = np.shape(do)[1], np.shape(k)[1]
+    hk = _kv_head(h, Hq, Hkv)
+    kk = np.asarray(k[b, hk], dtype=np.float64)
+    vv = np.asarray(v[b, hk], dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    Tq = q.shape[0]
+    p, _ = row_probs(q[rows], kk, scale, rows, Tq, causal)
+    g = np.asarray(do[b, h], dtype=np.float64)[rows]
+    dp = g @ vv.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ kk)
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float, heads=None):
+    """One query token per (batch, head) against the first seq_lens[b] cached keys.
+
+    q [B,Hq,d]; caches [B,Hkv,Tk_max,d]. Returns O [B,Hq,d] and LSE [B,Hq];
+    `heads` optionally limits the work to a list of (b, hq) pairs (others 0)."""
+    B, Hq, d = np.shape(q)
+    Hkv = np.shape(k_cache)[1]
+    o = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
+    for b, h in pairs:
+        L = int(seq_lens[b])
+        hk = _kv_head(h, Hq, Hkv)
+        kk = np.asarray(k_cache[b, hk, :L], dtype=np.float64)
+        vv = np.asarray(v_cache[b, hk, :L], dtype=np.float64)
+        qq = np.asarray(q[b, h], dtype=np.float64)[None, :]
+        p, l = row_probs(qq, kk, scale, np.zeros(1, dtype=np.int64), 1, False)
+        o[b, h] = (p @ vv)[0]
+        lse[b, h] = l[0]
+    return o, lse

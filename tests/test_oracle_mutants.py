@@ -1,0 +1,96 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and show that
+the pins reject every one of them.
+
+Each mutant is the oracle's own source with one textual edit, executed as a
+separate module; the real oracle is never modified.
+"""
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+from oracle import attention_ref as ref
+from tests import oracle_pins as pins
+
+
+def _mutant(old: str, new: str) -> types.ModuleType:
+    src = inspect.getsource(ref)
+    assert old in src, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _fails_some_forward_pin(mod) -> bool:
+    for pin in pins.ALL_FWD_PINS:
+        try:
+            pin(mod.attention_fwd)
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+FWD_MUTANTS = {
+    "scale dropped": ("s = scale * (q_rows @ k.T)", "s = q_rows @ k.T"),
+    "keys reversed": ("s = scale * (q_rows @ k.T)", "s = scale * (q_rows @ k[::-1].T)"),
+    "diagonal excluded": ("return j[None, :] <= rows[:, None] + (Tk - Tq)", "return j[None, :] < rows[:, None] + (Tk - Tq)"),
+    "top-left causal alignment": ("return j[None, :] <= rows[:, None] + (Tk - Tq)", "return j[None, :] <= rows[:, None]"),
+    "max missing from lse": ("lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))", "lse = np.where(empty, -np.inf, np.log(l_safe))"),
+    "not normalised": ("p = e / l_safe[:, None]", "p = e"),
+    "wrong kv head map": ("return hq // (Hq // Hkv)", "return hq % Hkv"),
+    "values swapped for keys": ("o[b, h, s:s + _ROW_BLOCK] = p @ v[b, hk]", "o[b, h, s:s + _ROW_BLOCK] = p @ k[b, hk]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FWD_MUTANTS))
+def test_forward_mutant_is_caught(name):
+    assert _fails_some_forward_pin(_mutant(*FWD_MUTANTS[name])), name
+
+
+def _fd_check(mod) -> bool:
+    """True when the mutant's backward agrees with central differences of the
+    (unmodified) forward on a small GQA causal case and a non-causal one."""
+    for causal, dims in ((True, (1, 4, 2, 4, 5, 3)), (False, (1, 2, 2, 3, 4, 2))):
+        B, Hq, Hkv, Tq, Tk, d = dims
+        rng = np.random.Generator(np.random.PCG64(99))
+        q = rng.standard_normal((B, Hq, Tq, d))
+        k = rng.standard_normal((B, Hkv, Tk, d))
+        v = rng.standard_normal((B, Hkv, Tk, d))
+        do = rng.standard_normal((B, Hq, Tq, d))
+        try:
+            grads = mod.attention_bwd(q, k, v, do, 0.9, causal)
+        except (ValueError, IndexError):
+            return False
+        for x, g in zip((q, k, v), grads):
+            if g.shape != x.shape:
+                return False
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + 1e-6
+                lp = np.sum(ref.attention_fwd(q, k, v, 0.9, causal)[0] * do)
+                x[idx] = old - 1e-6
+                lm = np.sum(ref.attention_fwd(q, k, v, 0.9, causal)[0] * do)
+                x[idx] = old
+                if abs((lp - lm) / 2e-6 - g[idx]) > 1e-6 + 1e-6 * abs(g[idx]):
+                    return False
+    return True
+
+
+BWD_MUTANTS = {
+    "row term dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "row term sign": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * (dp + (p * dp).sum(axis=1, keepdims=True))"),
+    "dq scale dropped": ("dq[b, h, r] = scale * (ds @ k[b, hk])", "dq[b, h, r] = ds @ k[b, hk]"),
+    "dk uses dO": ("dk[b, hk] += scale * (ds.T @ q[b, h, r])", "dk[b, hk] += scale * (ds.T @ g)"),
+    "dv overwritten per group": ("dv[b, hk] += p.T @ g", "dv[b, hk] = p.T @ g"),
+    "dp not transposed": ("dp = g @ v[b, hk].T", "dp = g @ v[b, hk][::-1].T"),
+}
+
+
+def test_unmutated_backward_passes_fd():
+    assert _fd_check(ref)
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    assert not _fd_check(_mutant(*BWD_MUTANTS[name])), name
