@@ -1,0 +1,159 @@
+/*
+ * fa.h -- C ABI of the exact tiled-attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact softmax attention
+ *     O = softmax(scale * Q K^T [+ causal mask]) V
+ * tile by tile with the online-softmax recurrence: per query row a running
+ * maximum m, a running sum l of exponentials taken relative to m, and a
+ * running value-weighted sum u, with l and u rescaled together by e^(m - m')
+ * whenever the maximum grows to m'. The T x T score and probability matrices
+ * never reach device memory.
+ *   kgptalkie "Flash Attention: Why Memory Traffic, Not Compute, Is the
+ *   Bottleneck", sections "Flash Attention Uses Tiles", "Softmax Looks Like an
+ *   Obstacle" and "Causal Masks Still Apply";
+ *   aimlrounds "FlashAttention", section "Softmax without seeing the whole
+ *   row" and the "FlashAttention 1, 2, 3" table (recomputation in the backward
+ *   pass, split-KV decoding).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major ("contiguous") device buffers owned by the
+ *     caller. bf16 tensors hold raw bfloat16 bit patterns (2 bytes each).
+ *       q, o, dout, dq : [B, Hq,  Tq, d]
+ *       k, v, dk, dv   : [B, Hkv, Tk, d]
+ *       lse            : [B, Hq,  Tq]  fp32, natural-log log-sum-exp of the
+ *                        scaled, masked scores of each query row.
+ *   - Grouped KV heads: query head h reads KV head h / (Hq / Hkv); Hq must be
+ *     a multiple of Hkv (Hq == Hkv is ordinary multi-head attention).
+ *   - causal != 0 masks key j for query i unless j <= i + (Tk - Tq): the
+ *     diagonal is aligned to the bottom-right corner, which is the ordinary
+ *     "query i sees keys 0..i" rule when Tq == Tk. A query that sees no key
+ *     (only possible when causal and Tq > Tk) gets O = 0 and LSE = -inf.
+ *   - scale multiplies Q K^T and must be finite and > 0 (typically 1/sqrt(d)).
+ *   - d must be 64 or 128. Every pointer must be 16-byte aligned.
+ *   - Every call is asynchronous on `stream` (0 = the null stream); results
+ *     are valid once the stream has completed. The library never allocates,
+ *     frees or synchronises, and keeps no global mutable state: concurrent
+ *     calls on different streams are safe when their outputs do not overlap.
+ *   - Argument checks run on the host before anything is enqueued: when a
+ *     call returns an error, nothing was launched and no output was touched.
+ *     FA_ERR_HIP reports a launch failure seen by hipGetLastError afterwards.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, bad scale */
+  FA_ERR_UNSUPPORTED = -2,   /* head width other than 64 or 128 */
+  FA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  FA_ERR_HIP = -4            /* a kernel launch failed */
+} fa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Forward pass, bf16 inputs and outputs, fp32 accumulation.
+ *   q [B,Hq,Tq,d], k and v [B,Hkv,Tk,d]  (bf16, read only)
+ *   o [B,Hq,Tq,d]                        (bf16, written)
+ *   lse [B,Hq,Tq] fp32, written when non-NULL; it is what fa_bwd needs to
+ *   recompute the probabilities (aimlrounds "FlashAttention": one fp32
+ *   log-sum-exp per row and head is kept for the backward pass).
+ * QK^T and PV run on bf16 matrix cores; the probabilities are rounded to bf16
+ * before the PV product, the running sum uses them unrounded.
+ * Errors: FA_ERR_INVALID_ARG (q/k/v/o NULL, any size <= 0, Hq % Hkv != 0,
+ * scale not finite or <= 0, misaligned pointer), FA_ERR_UNSUPPORTED (d).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+           hipStream_t stream);
+
+/*
+ * Forward pass with fp32 inputs and outputs (same parameter list and layout
+ * as fa_fwd, every tensor fp32). Scores, probabilities and accumulators stay
+ * in fp32 throughout: this is the accuracy reference path for small problems
+ * and the pages' worked rows, not a throughput path. Same errors as fa_fwd.
+ */
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+               hipStream_t stream);
+
+/*
+ * Workspace bytes fa_bwd needs: one fp32 per query row for
+ * D_i = sum_c dO_ic O_ic, rounded up to 256 bytes. Linear in Tq, never
+ * quadratic (aimlrounds "FlashAttention": the N x N matrix is not stored).
+ * Returns 0 for non-positive sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d);
+
+/*
+ * Backward pass by recomputation (bf16 tensors, fp32 accumulation).
+ *   q, k, v        forward inputs                        (bf16, read only)
+ *   o              forward output from fa_fwd            (bf16, read only)
+ *   dout           gradient of the loss w.r.t. o          (bf16, read only)
+ *   lse            log-sum-exp written by fa_fwd          (fp32, read only)
+ *   dq [B,Hq,Tq,d], dk and dv [B,Hkv,Tk,d]                (bf16, written;
+ *                  dk and dv sum over the query heads of each KV group)
+ *   workspace      device scratch of at least fa_bwd_workspace_size() bytes
+ * The probabilities are rebuilt tile by tile from Q, K and lse instead of
+ * being read back (aimlrounds "FlashAttention", follow-up on why the backward
+ * pass recomputes; zerotofrontier "Efficient attention: memory-bound",
+ * section "Real code moves even more", for the products dV = P^T dO,
+ * dP = dO V^T, dS from P and dP, dQ and dK from dS). With
+ * dS_ij = P_ij (dP_ij - D_i): dQ = scale dS K, dK = scale dS^T Q.
+ * The result is deterministic (no atomics). Errors: as fa_fwd, plus
+ * FA_ERR_INVALID_ARG for NULL o/dout/lse/dq/dk/dv and FA_ERR_WORKSPACE.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+           hipStream_t stream);
+
+/*
+ * Workspace bytes fa_decode_splitkv needs for KV caches of up to Tk_max
+ * positions: per (batch, query head, split) one partial state (m, l, u[d])
+ * in fp32, for the largest split count the library may choose. Linear in
+ * Tk_max. Returns 0 for non-positive sizes.
+ */
+size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d);
+
+/*
+ * One query token per (batch, query head) against a KV cache (split-KV
+ * decoding, aimlrounds "FlashAttention", note under the "FlashAttention 1,
+ * 2, 3" table: the long cache is split across workgroups).
+ *   q [B,Hq,d]                 (bf16, read only)
+ *   k_cache, v_cache [B,Hkv,Tk_max,d]  (bf16, read only; positions at or
+ *                              beyond seq_lens[b] are never read)
+ *   seq_lens [B]               (int32, device memory) valid cache lengths
+ *   o [B,Hq,d]                 (bf16, written)
+ *   lse [B,Hq]                 (fp32, written when non-NULL)
+ *   workspace                  fp32 partial states, >= fa_decode_workspace_size
+ *   chunk                      keys per split: 0 lets the library choose,
+ *                              otherwise a multiple of 64 in [64, Tk_max
+ *                              rounded up to 64]
+ * Each split runs the online recurrence over its keys and stores its partial
+ * (m, l, u); a second kernel merges the splits with the same rescale rule.
+ * Device-side range errors: a seq_lens[b] outside [1, Tk_max] cannot be
+ * reported without a synchronisation; that batch entry's o (and lse) are
+ * written as NaN instead. Errors: FA_ERR_INVALID_ARG (NULL q/k_cache/v_cache/
+ * seq_lens/o, sizes, Hq % Hkv, scale, chunk), FA_ERR_UNSUPPORTED (d),
+ * FA_ERR_WORKSPACE.
+ */
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, void* o, float* lse,
+                      void* workspace, size_t ws_bytes,
+                      int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,166 @@
+// fa_api.cpp -- the C ABI: argument checks on the host, then kernel launches.
+// Every check happens before anything is enqueued, so an error return means
+// no kernel ran and no output was touched.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kMaxGrid = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // element offsets are formed in size_t, row indices in int
+  if ((int64_t)B * Hq > INT32_MAX / 2 || (int64_t)B * Hkv > INT32_MAX / 2) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+           hipStream_t stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if ((int64_t)((Tq + 127) / 128) * B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.c = scale * fa::kLog2eHost;
+  return to_status(fa::launch_fwd_bf16(a, d, causal != 0, stream));
+}
+
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+               hipStream_t stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if ((int64_t)((Tq + 63) / 64) * B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  fa::FwdF32Args a{};
+  a.q = static_cast<const float*>(q);
+  a.k = static_cast<const float*>(k);
+  a.v = static_cast<const float*>(v);
+  a.o = static_cast<float*>(o);
+  a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.scale = scale;
+  return to_status(fa::launch_fwd_f32(a, d, causal != 0, stream));
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d) {
+  if (B <= 0 || Hq <= 0 || Tq <= 0 || d <= 0) return 0;
+  return round256((size_t)B * Hq * Tq * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+           hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || ws_bytes < fa_bwd_workspace_size(B, Hq, Tq, d))
+    return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(workspace);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.scale = scale;
+  a.c = scale * fa::kLog2eHost;
+  return to_status(fa::launch_bwd(a, d, causal != 0, stream));
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d) {
+  if (B <= 0 || Hq <= 0 || Tk_max <= 0 || d <= 0) return 0;
+  const size_t splits = ((size_t)Tk_max + fa::kDecodeMinChunk - 1) / fa::kDecodeMinChunk;
+  const size_t per = (size_t)B * Hq * splits;
+  return round256(per * sizeof(float)) * 2 + round256(per * d * sizeof(float));
+}
+
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, void* o, float* lse,
+                      void* workspace, size_t ws_bytes,
+                      int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
+                      hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !o) return FA_ERR_INVALID_ARG;
+  const int st = check_common(B, Hq, Hkv, 1, Tk_max, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  if (chunk == 0) chunk = fa::kDecodeAutoChunk;
+  if (chunk < fa::kDecodeMinChunk || chunk % 64 != 0) return FA_ERR_INVALID_ARG;
+  const int max_chunk = (Tk_max + 63) / 64 * 64;
+  if (chunk > max_chunk) chunk = max_chunk;
+  const int n_splits = (Tk_max + chunk - 1) / chunk;
+  const int G = Hq / Hkv;
+  if (B > kMaxGrid || (int64_t)Hkv * ((G + 15) / 16) > kMaxGrid) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || ws_bytes < fa_decode_workspace_size(B, Hq, Tk_max, d))
+    return FA_ERR_WORKSPACE;
+  const size_t per_full = (size_t)B * Hq * (((size_t)Tk_max + fa::kDecodeMinChunk - 1) / fa::kDecodeMinChunk);
+  fa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.seq_lens = seq_lens;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(ws);
+  a.part_l = reinterpret_cast<float*>(ws + round256(per_full * sizeof(float)));
+  a.part_u = reinterpret_cast<float*>(ws + 2 * round256(per_full * sizeof(float)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tk_max = Tk_max;
+  a.chunk = chunk;
+  a.n_splits = n_splits;
+  a.c = scale * fa::kLog2eHost;
+  return to_status(fa::launch_decode(a, d, stream));
+}
+
+}  // extern "C"

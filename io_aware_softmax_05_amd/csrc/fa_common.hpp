@@ -1,0 +1,99 @@
+// fa_common.hpp -- gfx950 building blocks shared by the attention kernels.
+//
+// Matrix-core conventions (measured on gfx950, 64-lane waves):
+//   v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] * B[16x32]
+//     lane l holds A[l%32][8*(l/32) + e] and B[8*(l/32) + e][l%32], e = 0..7,
+//     and D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator register r = 0..15.
+//   v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16]
+//     lane l holds A[l%16][8*(l/16) + e], B[8*(l/16) + e][l%16], and
+//     D[4*(l/16) + r][l%16] in register r = 0..3.
+//   ds_read_b64_tr_b16: inside each 16-lane group, lane i names a row R_i of
+//     four 16-bit values; lane j receives R_{4t + j/4}[j%4] as element t.
+//   v_permlane32_swap (x, x): returns {x[l%32], x[32 + l%32]} in every lane l.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (exact 0 for -inf).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit.
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// max / sum of x over lanes l and l^32 (the two lanes that share a column of
+// a 32x32 accumulator), returned in both.
+__device__ __forceinline__ float pair_max32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two fp32 -> packed bf16 pair (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transposed 4 x 16-bit read (see header comment), from an LDS byte offset.
+__device__ __forceinline__ u32x2 lds_read_tr(const FA_LDS uint8_t* base, uint32_t byte_off) {
+  auto p = (FA_LDS s16x4*)(base + byte_off);
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(const FA_LDS uint8_t* base, uint32_t byte_off) {
+  return *(const FA_LDS u32x4*)(base + byte_off);
+}
+
+__device__ __forceinline__ void lds_write_b128(FA_LDS uint8_t* base, uint32_t byte_off, u32x4 v) {
+  *(FA_LDS u32x4*)(base + byte_off) = v;
+}
+
+__device__ __forceinline__ u32x4 global_load_b128(const void* p) {
+  return *(const u32x4*)p;
+}
+
+// Workgroup index remap so that consecutive logical tiles share one XCD.
+// Hardware deals workgroups round-robin over the 8 XCDs (id % 8); logical
+// tile t is placed on XCD t / ceil-share, which keeps the tiles of one head
+// (and their K/V stream) inside one XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t per = n / kXcd, rem = n % kXcd;
+  const uint32_t x = bid % kXcd, k = bid / kXcd;
+  return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+}  // namespace fa

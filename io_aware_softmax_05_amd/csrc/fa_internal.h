@@ -1,0 +1,73 @@
+// fa_internal.h -- launch interfaces between the C ABI layer and the kernels.
+// Every launcher assumes its arguments were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const uint16_t* q;  // [B,Hq,Tq,d] bf16
+  const uint16_t* k;  // [B,Hkv,Tk,d] bf16
+  const uint16_t* v;  // [B,Hkv,Tk,d] bf16
+  uint16_t* o;        // [B,Hq,Tq,d] bf16
+  float* lse;         // [B,Hq,Tq] or null
+  int B, Hq, Hkv, Tq, Tk;
+  float c;            // scale * log2(e)
+  int n_qtiles;       // filled in by the launcher
+};
+
+struct FwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, Tq, Tk;
+  float scale;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;        // [B,Hq,d]
+  const uint16_t* k;        // [B,Hkv,Tk_max,d]
+  const uint16_t* v;        // [B,Hkv,Tk_max,d]
+  const int* seq_lens;      // [B]
+  uint16_t* o;              // [B,Hq,d]
+  float* lse;               // [B,Hq] or null
+  float* part_m;            // [B,Hq,S]   running max, log2 units
+  float* part_l;            // [B,Hq,S]   running sum
+  float* part_u;            // [B,Hq,S,d] weighted sum
+  int B, Hq, Hkv, Tk_max;
+  int chunk;                // keys per split (multiple of 64)
+  int n_splits;             // ceil(Tk_max / chunk)
+  float c;                  // scale * log2(e)
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;         // natural log
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;             // [B,Hq,Tq] workspace: rowsum(dO * O)
+  int B, Hq, Hkv, Tq, Tk;
+  float scale;
+  float c;                  // scale * log2(e)
+};
+
+hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(FwdF32Args a, int d, bool causal, hipStream_t stream);
+hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream);
+hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream);
+
+constexpr float kLog2eHost = 1.44269504088896340736f;
+constexpr int kDecodeMinChunk = 64;
+constexpr int kDecodeAutoChunk = 512;
+
+}  // namespace fa

@@ -1,0 +1,216 @@
+"""Thin ctypes binding over the C ABI in include/fa.h (libfa_gfx950.so).
+
+The functions named like the C entry points (fa_fwd, fa_fwd_f32, fa_bwd,
+fa_decode_splitkv, the workspace-size queries, fa_status_string) take the C
+parameter list as-is -- device tensors stand in for pointers -- and only
+marshal arguments; a non-zero status raises FaError. The lower-case helpers
+(forward, backward, decode) additionally check shapes and dtypes and allocate
+outputs with torch; every arithmetic step runs in the library's kernels.
+
+torch is used for device memory and streams only. It is imported before the
+library is loaded so that both share one HIP runtime. There is no fallback:
+if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa_gfx950.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_WORKSPACE = -3
+FA_ERR_HIP = -4
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+# (restype, argtypes) per exported symbol, in header order.
+_SIGNATURES = {
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_decode_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {status_string(status)} ({status})")
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fa_[a-z0-9_]+)\s*\(", text, flags=re.M)
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle; raises LibraryMissing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise LibraryMissing(f"{p} is not built; run io_aware_softmax_05_amd.build.build_library()")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().fa_status_string(int(status)).decode()
+    except LibraryMissing:
+        return f"status {status}"
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+# ------------------------------------------------------------ C entry points
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream=None) -> None:
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
+                               float(scale), int(bool(causal)), _stream(stream))
+    _check(st, "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream=None) -> None:
+    st = load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
+                                   float(scale), int(bool(causal)), _stream(stream))
+    _check(st, "fa_fwd_f32")
+
+
+def fa_bwd_workspace_size(B, Hq, Tq, d) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, Hq, Tq, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, causal,
+           stream=None) -> None:
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tq, Tk, d, float(scale),
+                               int(bool(causal)), _stream(stream))
+    _check(st, "fa_bwd")
+
+
+def fa_decode_workspace_size(B, Hq, Tk_max, d) -> int:
+    return int(load_library().fa_decode_workspace_size(B, Hq, Tk_max, d))
+
+
+def fa_decode_splitkv(q, k_cache, v_cache, seq_lens, o, lse, workspace, ws_bytes, B, Hq, Hkv, Tk_max, d,
+                      scale, chunk=0, stream=None) -> None:
+    st = load_library().fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(o),
+                                          _ptr(lse), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tk_max, d,
+                                          float(scale), int(chunk), _stream(stream))
+    _check(st, "fa_decode_splitkv")
+
+
+# ------------------------------------------------ tensor-level conveniences
+
+def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor with {ndim} dims, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, with_lse: bool = True, stream=None):
+    """O (and LSE) for q [B,Hq,Tq,d], k and v [B,Hkv,Tk,d]; bf16 or fp32."""
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, dt, 4, name)
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must both be [B,Hkv,Tk,d] matching q")
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if with_lse else None
+    fn = fa_fwd if dt == torch.bfloat16 else fa_fwd_f32 if dt == torch.float32 else None
+    if fn is None:
+        raise ValueError(f"unsupported dtype {dt}")
+    fn(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None):
+    """dQ, dK, dV (bf16) by recomputation from the saved LSE."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, torch.bfloat16, 4, name)
+    _need(lse, torch.float32, 3, "lse")
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    scale = d ** -0.5 if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa_bwd_workspace_size(B, Hq, Tq, d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream)
+    return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, chunk: int = 0, workspace=None,
+           stream=None):
+    """O [B,Hq,d] and LSE [B,Hq] for one query token per head."""
+    _need(q, torch.bfloat16, 3, "q")
+    _need(k_cache, torch.bfloat16, 4, "k_cache")
+    _need(v_cache, torch.bfloat16, 4, "v_cache")
+    _need(seq_lens, torch.int32, 1, "seq_lens")
+    B, Hq, d = q.shape
+    Hkv, Tk_max = k_cache.shape[1], k_cache.shape[2]
+    scale = d ** -0.5 if scale is None else scale
+    ws_bytes = fa_decode_workspace_size(B, Hq, Tk_max, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    fa_decode_splitkv(q, k_cache, v_cache, seq_lens, o, lse, workspace, workspace.numel(), B, Hq, Hkv, Tk_max, d,
+                      scale, chunk, stream)
+    return o, lse

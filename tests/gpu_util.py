@@ -1,0 +1,72 @@
+"""Helpers for the GPU parity tests: moving seeded inputs to the device and
+the tolerance rules the HIP path must meet against the fp64 oracle.
+
+Tolerances (written here, used by every GPU test):
+  * fp32 path: max |x - ref| <= 1e-5, taken relative to max(1, |ref|) so that
+    the pages' worked rows (|O| ~ 62) get the same ~2-3 fp32 ulps;
+  * bf16 path: max |x - ref| <= 2e-2 and ||x - ref||_2 / ||ref||_2 <= 1e-2 for
+    every output tensor (the relative term keeps the check meaningful when
+    |O| ~ sqrt(e/T) is small);
+  * LSE: max |x - ref| <= 1e-4 (bf16 inputs), <= 1e-5 (fp32 inputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from io_aware_softmax_05_amd import inputs
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def report(name: str, got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{name}: non-finite pattern differs"
+    diff = np.where(fin, got - np.where(fin, ref, 0), 0.0)
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(np.where(fin, ref, 0)))
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else max_abs
+    print(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    return max_abs, rel
+
+
+def check_bf16(name: str, got, ref) -> None:
+    got = host(got) if isinstance(got, torch.Tensor) else got
+    max_abs, rel = report(name, got, ref)
+    assert max_abs <= 2e-2 and rel <= 1e-2, f"{name}: max_abs={max_abs:.3e} rel={rel:.3e}"
+
+
+def check_f32(name: str, got, ref) -> None:
+    got = host(got) if isinstance(got, torch.Tensor) else got
+    report(name, got, ref)
+    fin = np.isfinite(ref)
+    err = np.abs(np.where(fin, got - np.where(fin, ref, 0), 0.0)) / np.maximum(1.0, np.abs(np.where(fin, ref, 0)))
+    assert float(err.max(initial=0.0)) <= 1e-5, f"{name}: scaled max err {float(err.max()):.3e}"
+
+
+def check_lse(name: str, got, ref, tol: float) -> None:
+    got = host(got) if isinstance(got, torch.Tensor) else got
+    max_abs, _ = report(name, got, ref)
+    assert max_abs <= tol, f"{name}: max_abs={max_abs:.3e} > {tol}"
+
+
+def attention_case(seed, B, Hq, Hkv, Tq, Tk, d, dtype="bf16", with_dout=False, q_gain=1.0):
+    """Seeded inputs (numpy, exact values) and their device copies."""
+    x = inputs.draw_attention_inputs(seed, B, Hq, Hkv, Tq, Tk, d, dtype, with_dout)
+    if q_gain != 1.0:
+        qv = inputs.widen(x["q"]) * q_gain     # exact: a power-of-two gain keeps bf16 values exact
+        x["q"] = inputs.bf16_bits_from_f32(qv.astype(np.float32)) if dtype == "bf16" else qv.astype(np.float32)
+    host_vals = {n: inputs.widen(a) for n, a in x.items()}
+    to_dev = dev_bf16 if dtype == "bf16" else dev_f32
+    dev = {n: to_dev(a) for n, a in x.items()}
+    return host_vals, dev

@@ -1,0 +1,192 @@
+"""GPU parity of the forward entry points (fa_fwd bf16, fa_fwd_f32) against the
+fp64 oracle, through the C ABI. Tolerances are those in tests/gpu_util.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from io_aware_softmax_05_amd import fa, inputs
+from oracle import attention_ref as ref
+from tests import gpu_util as gu
+from tests import oracle_pins as pins
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd(dev, causal, scale, dtype="bf16"):
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    fn = fa.fa_fwd if dtype == "bf16" else fa.fa_fwd_f32
+    fn(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ----------------------------------------------------------------- fp32 path
+
+@pytest.mark.parametrize("row", ["four_key_row", "eight_key_row"])
+def test_worked_rows_fp32(row):
+    g = pins.load_worked_rows()[row]
+    print(f"[worked row {row}]", flush=True)
+    q, k, v = pins.embed_row(g["scores"], g["values"], d=64)
+    dev = {n: gu.dev_f32(a) for n, a in (("q", q), ("k", k), ("v", v))}
+    o, lse = _fwd(dev, False, 1.0, "f32")
+    o_ref, lse_ref = ref.attention_fwd(q, k, v, 1.0, False)
+    gu.check_f32("O", o, o_ref)
+    gu.check_lse("LSE", lse, lse_ref, 1e-5)
+    if row == "eight_key_row":
+        assert abs(float(o[0, 0, 0, 0]) - g["final_output"]) <= 0.005
+    else:
+        l2, u2 = pins.closed_form_four_key()
+        assert math.isclose(float(o[0, 0, 0, 0]), u2 / l2, rel_tol=1e-6)
+
+
+def test_single_head_fp32_workload():
+    """B1 H1 T256 d64 fp32, seed 1, non-causal, scale 1/8."""
+    w = inputs.WORKLOADS[1]
+    print(f"[{w.name}]", flush=True)
+    hv, dev = gu.attention_case(w.seed, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, "f32")
+    o, lse = _fwd(dev, w.causal, w.scale, "f32")
+    o_ref, lse_ref = ref.attention_fwd(hv["q"], hv["k"], hv["v"], w.scale, w.causal)
+    gu.check_f32("O", o, o_ref)
+    gu.check_lse("LSE", lse, lse_ref, 1e-5)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 70, 100, 128, True), (1, 2, 2, 90, 40, 64, True),
+                                   (2, 2, 1, 65, 33, 64, False)])
+def test_fp32_edges(shape):
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    print(f"[fp32 {shape}]", flush=True)
+    hv, dev = gu.attention_case(11, B, Hq, Hkv, Tq, Tk, d, "f32")
+    o, lse = _fwd(dev, causal, d ** -0.5, "f32")
+    o_ref, lse_ref = ref.attention_fwd(hv["q"], hv["k"], hv["v"], d ** -0.5, causal)
+    gu.check_f32("O", o, o_ref)
+    gu.check_lse("LSE", lse, lse_ref, 1e-5)
+
+
+# ----------------------------------------------------------------- bf16 path
+
+BF16_SHAPES = [
+    (2, 4, 4, 300, 300, 64, False),
+    (2, 4, 4, 300, 300, 64, True),
+    (1, 4, 2, 257, 257, 128, True),
+    (1, 4, 4, 256, 256, 128, False),
+    (1, 8, 1, 200, 333, 128, True),     # Tq < Tk, 8 query heads per KV head
+    (1, 2, 2, 150, 100, 64, True),      # Tq > Tk: the first 50 rows see no key
+    (1, 2, 2, 1, 77, 128, False),
+    (1, 2, 2, 17, 17, 128, True),
+    (3, 2, 1, 63, 1000, 64, False),
+    (1, 2, 2, 255, 64, 128, False),
+]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_parity(shape):
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    print(f"[bf16 {shape}]", flush=True)
+    hv, dev = gu.attention_case(100 + Tq, B, Hq, Hkv, Tq, Tk, d)
+    scale = d ** -0.5
+    o, lse = _fwd(dev, causal, scale)
+    o_ref, lse_ref = ref.attention_fwd(hv["q"], hv["k"], hv["v"], scale, causal)
+    gu.check_bf16("O", o, o_ref)
+    gu.check_lse("LSE", lse, lse_ref, 1e-4)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+def test_bf16_peaky_scores(d, causal):
+    """Queries scaled by 8 give scores with sigma ~ 8, so the running maximum
+    moves a lot between tiles and max-abs errors are not hidden by small O."""
+    print(f"[peaky d={d} causal={causal}]", flush=True)
+    hv, dev = gu.attention_case(7, 1, 4, 2, 333, 333, d, q_gain=8.0)
+    o, lse = _fwd(dev, causal, d ** -0.5)
+    o_ref, lse_ref = ref.attention_fwd(hv["q"], hv["k"], hv["v"], d ** -0.5, causal)
+    gu.check_bf16("O", o, o_ref)
+    gu.check_lse("LSE", lse, lse_ref, 1e-3)
+
+
+def test_bf16_deterministic_and_lse_optional():
+    hv, dev = gu.attention_case(9, 2, 4, 2, 400, 400, 128)
+    o1, l1 = _fwd(dev, True, 0.1)
+    o2, l2 = _fwd(dev, True, 0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    o3 = torch.empty_like(q)
+    fa.fa_fwd(q, k, v, o3, None, 2, 4, 2, 400, 400, 128, 0.1, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3)
+
+
+def test_bf16_nan_poisoned_padding():
+    """Inputs sit at the front of NaN-filled buffers and the output buffer has
+    a sentinel tail: nothing past a tensor's end is read or written."""
+    B, Hq, Hkv, Tq, Tk, d = 1, 2, 1, 130, 70, 128
+    hv, dev = gu.attention_case(5, B, Hq, Hkv, Tq, Tk, d)
+    pad = 4096
+
+    def padded(t):
+        buf = torch.full((t.numel() + pad,), float("nan"), dtype=t.dtype, device=t.device)
+        buf[: t.numel()] = t.reshape(-1)
+        return buf, buf[: t.numel()].view(t.shape)
+
+    _, q = padded(dev["q"])
+    _, k = padded(dev["k"])
+    _, v = padded(dev["v"])
+    obuf = torch.full((dev["q"].numel() + pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = obuf[: dev["q"].numel()].view(dev["q"].shape)
+    lbuf = torch.full((B * Hq * Tq + 64,), 7.0, dtype=torch.float32, device="cuda")
+    lse = lbuf[: B * Hq * Tq].view(B, Hq, Tq)
+    for causal in (False, True):
+        fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, d ** -0.5, causal)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = ref.attention_fwd(hv["q"], hv["k"], hv["v"], d ** -0.5, causal)
+        gu.check_bf16("O", o, o_ref)
+        gu.check_lse("LSE", lse, lse_ref, 1e-4)
+        assert torch.all(obuf[dev["q"].numel():] == 7.0)
+        assert torch.all(lbuf[B * Hq * Tq:] == 7.0)
+
+
+# --------------------------------------------------- full workload sizes
+
+def _sampled_rows_check(w, dev, raw, rows_per_head, heads):
+    o, lse = _fwd(dev, w.causal, w.scale)
+    o_h, lse_h = gu.host(o), lse.cpu().numpy()
+    g = w.Hq // w.Hkv
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for (b, h) in heads:
+        rows = rows_per_head
+        q = inputs.widen(raw["q"][b, h, rows])
+        k = inputs.widen(raw["k"][b, h // g])
+        v = inputs.widen(raw["v"][b, h // g])
+        p, l = ref.row_probs(q, k, w.scale, np.asarray(rows), w.Tq, w.causal)
+        ref_o.append(p @ v)
+        ref_l.append(l)
+        got_o.append(o_h[b, h, rows])
+        got_l.append(lse_h[b, h, rows])
+    gu.check_bf16("O (sampled rows)", np.concatenate(got_o), np.concatenate(ref_o))
+    gu.check_lse("LSE (sampled rows)", np.concatenate(got_l), np.concatenate(ref_l), 1e-4)
+
+
+def _edge_rows(T, n_random, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = [0, 1, 63, 64, 127, 128, 129, T // 2, T - 129, T - 128, T - 2, T - 1]
+    return sorted(set([r for r in fixed if 0 <= r < T] + rng.integers(0, T, n_random).tolist()))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_full_size_forward_sampled(n):
+    """The forward at the workloads' full sizes (GPT-2-medium B64 H16 T1024 d64;
+    causal B1 H32 T8192 d128; causal GQA B1 Hq32 Hkv8 T32768 d128), checked on
+    sampled rows that the oracle evaluates one by one."""
+    w = inputs.WORKLOADS[n]
+    print(f"[full size fwd: {w.name}]", flush=True)
+    raw = inputs.draw_attention_inputs(w.seed, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.dtype, False)
+    dev = {n_: gu.dev_bf16(a) for n_, a in raw.items()}
+    rng = np.random.Generator(np.random.PCG64(n))
+    heads = sorted({(int(rng.integers(0, w.B)), int(rng.integers(0, w.Hq))) for _ in range(4)} |
+                   {(0, 0), (w.B - 1, w.Hq - 1)})
+    _sampled_rows_check(w, dev, raw, _edge_rows(w.Tq, 20, n), heads)
