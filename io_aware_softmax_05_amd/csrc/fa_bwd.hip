@@ -1,5 +1,458 @@
+// fa_bwd.hip -- backward pass of exact attention by recomputation.
+//
+// The probabilities are never stored: each kernel rebuilds P tile by tile
+// from Q, K and the fp32 log-sum-exp the forward saved (aimlrounds
+// "FlashAttention", follow-up on why the backward pass recomputes instead of
+// storing P). The products are the ones of the standard backward
+// (zerotofrontier "Efficient attention: memory-bound", section "Real code
+// moves even more"): dV = P^T dO, dP = dO V^T, dS from P and dP, dQ and dK
+// from dS, with the softmax Jacobian dS_ij = P_ij (dP_ij - D_i) and
+// D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic.
+//
+// Three kernels, no atomics (the result is deterministic):
+//   pre   D_i = rowsum(dO * O) in fp32 (HBM bound, one pass over O and dO).
+//   dkdv  one workgroup per 128 keys of a KV head (32 keys per wave, K and V
+//         fragments held in registers); it walks every query tile of every
+//         query head of the group. S = Q K^T puts one key per lane, so P and
+//         dS feed dV^T = dO^T P and dK^T = Q^T dS straight from the
+//         accumulators; dO^T and Q^T come from ds_read_b64_tr_b16.
+//   dq    one workgroup per 128 query rows, laid out like the forward
+//         (S^T = K Q^T, one query per lane): dQ^T = K^T dS^T with K^T from
+//         transposed LDS reads.
 #include "fa_common.hpp"
 #include "fa_internal.h"
+
 namespace fa {
-hipError_t launch_bwd(BwdArgs, int, bool, hipStream_t) { return hipErrorNotSupported; }
+
+// ------------------------------------------------------------------ pre
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long n_rows) {
+  constexpr int LPR = D / 8;                   // lanes per row (16 B each)
+  constexpr int RPB = 256 / LPR;               // rows per block
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / LPR;
+  const int part = tid % LPR;
+  float acc = 0.f;
+  if (row < n_rows) {
+    const u32x4 o = global_load_b128(a.o + row * D + part * 8);
+    const u32x4 g = global_load_b128(a.dout + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(o[e]), bf16_lo(g[e]), acc);
+      acc = fmaf(bf16_hi(o[e]), bf16_hi(g[e]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < n_rows && part == 0) a.delta[row] = acc;
 }
+
+// ----------------------------------------------------------------- dk dv
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+  constexpr int BK = 128;                 // keys per workgroup
+  constexpr int BQ = 64;                  // query rows per tile
+  constexpr int PITCH = (D + 16) * 2;
+  constexpr int TILE = BQ * PITCH;        // one of Q / dO
+  constexpr int STATS = 2 * BQ * 4;       // lse2 and delta
+  constexpr int BUF = 2 * TILE + STATS;
+  constexpr int CH = D / 8;
+  constexpr int LOADS = BQ * CH / 256;
+  static_assert(LOADS * 256 == BQ * CH, "tile must split evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * BUF];
+  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = (int)(t % (uint32_t)n_ktiles);   // causal: small kt has the most work
+  const int bhk = (int)(t / (uint32_t)n_ktiles);
+  const int b = bhk / a.Hkv, hk = bhk - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int k0 = kt * BK;
+  const int key = k0 + wave * 32 + col;           // this lane's key
+  const int shift = a.Tk - a.Tq;
+  const size_t kvoff = (size_t)bhk * a.Tk * D;
+
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T.
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const bool live = key < a.Tk;
+    const uint16_t* ks = a.k + kvoff + (size_t)(live ? key : 0) * D + 8 * half;
+    const uint16_t* vs = a.v + kvoff + (size_t)(live ? key : 0) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kf[s] = as_bf16x8(live ? global_load_b128(ks + s * 16) : u32x4{0, 0, 0, 0});
+      vf[s] = as_bf16x8(live ? global_load_b128(vs + s * 16) : u32x4{0, 0, 0, 0});
+    }
+  }
+
+  f32x16 dv_acc[D / 32], dk_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dv_acc[db][r] = 0.f;
+      dk_acc[db][r] = 0.f;
+    }
+
+  // Query tiles that can see any key of this workgroup.
+  int qt_begin = 0;
+  if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
+  const int n_qt = (a.Tq + BQ - 1) / BQ;
+  const int per_head = max(0, n_qt - qt_begin);
+  const int n_iter = per_head * G;
+
+  u32x4 qst[LOADS], gst[LOADS];
+  float lse_st = 0.f, del_st = 0.f;
+  auto load_tile = [&](int it) {
+    const int hq = hk * G + it / per_head;
+    const int q0 = (qt_begin + it % per_head) * BQ;
+    const size_t qoff = ((size_t)b * a.Hq + hq) * a.Tq;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / CH, ch = c % CH;
+      const int qr = q0 + row;
+      if (qr < a.Tq) {
+        qst[i] = global_load_b128(a.q + (qoff + qr) * D + ch * 8);
+        gst[i] = global_load_b128(a.dout + (qoff + qr) * D + ch * 8);
+      } else {
+        qst[i] = u32x4{0, 0, 0, 0};
+        gst[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int qr = q0 + tid;
+      if (qr < a.Tq) {
+        const float l = a.lse[qoff + qr];
+        // a row with no visible key (LSE = -inf) must give P = 0
+        lse_st = l == -INFINITY ? INFINITY : l * kLog2e;
+        del_st = a.delta[qoff + qr];
+      } else {
+        lse_st = INFINITY;
+        del_st = 0.f;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    FA_LDS uint8_t* qb = smem + buf * BUF;
+    FA_LDS uint8_t* gb = qb + TILE;
+    FA_LDS float* st = (FA_LDS float*)(gb + TILE);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / CH, ch = c % CH;
+      lds_write_b128(qb, row * PITCH + ch * 16, qst[i]);
+      lds_write_b128(gb, row * PITCH + ch * 16, gst[i]);
+    }
+    if (tid < BQ) {
+      st[tid] = lse_st;
+      st[BQ + tid] = del_st;
+    }
+  };
+
+  if (n_iter > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const int grp = lane >> 4, gi = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_iter) load_tile(it + 1);
+    const FA_LDS uint8_t* qb = smem + buf * BUF;
+    const FA_LDS uint8_t* gb = qb + TILE;
+    const FA_LDS float* st = (const FA_LDS float*)(gb + TILE);
+    const int q0 = (qt_begin + it % per_head) * BQ;
+
+    // S = Q K^T and dP = dO V^T for 64 queries x 32 keys (one key per lane).
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qblk = 0; qblk < 2; ++qblk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[qblk][r] = 0.f;
+        dp[qblk][r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int off = (qblk * 32 + col) * PITCH + (ks * 16 + 8 * half) * 2;
+        s[qblk] = mfma32(as_bf16x8(lds_read_b128(qb, off)), kf[ks], s[qblk]);
+        dp[qblk] = mfma32(as_bf16x8(lds_read_b128(gb, off)), vf[ks], dp[qblk]);
+      }
+    }
+
+    const bool need_mask = CAUSAL && (q0 < k0 + wave * 32 + 31 - shift);
+    uint32_t pw[2][8], dsw[2][8];
+#pragma unroll
+    for (int qblk = 0; qblk < 2; ++qblk)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rq = qblk * 32 + 8 * g4 + 4 * half;   // first of 4 consecutive rows
+        const f32x4 l2 = *(const FA_LDS f32x4*)(st + rq);
+        const f32x4 dl = *(const FA_LDS f32x4*)(st + BQ + rq);
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pe = exp2_fast(fmaf(s[qblk][r], a.c, -l2[e]));
+          if (need_mask && key > q0 + rq + e + shift) pe = 0.f;
+          p[e] = pe;
+          ds[e] = pe * (dp[qblk][r] - dl[e]);
+        }
+        pw[qblk][2 * g4] = pack_bf16x2(p[0], p[1]);
+        pw[qblk][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
+        dsw[qblk][2 * g4] = pack_bf16x2(ds[0], ds[1]);
+        dsw[qblk][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+      }
+
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
+#pragma unroll
+    for (int qblk = 0; qblk < 2; ++qblk)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 pb = as_bf16x8(u32x4{pw[qblk][4 * hs], pw[qblk][4 * hs + 1],
+                                          pw[qblk][4 * hs + 2], pw[qblk][4 * hs + 3]});
+        const bf16x8 sb = as_bf16x8(u32x4{dsw[qblk][4 * hs], dsw[qblk][4 * hs + 1],
+                                          dsw[qblk][4 * hs + 2], dsw[qblk][4 * hs + 3]});
+        const int row = qblk * 32 + hs * 16 + tr_row;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int cb = (db * 32 + tr_col) * 2;
+          const u32x2 glo = lds_read_tr(gb, row * PITCH + cb);
+          const u32x2 ghi = lds_read_tr(gb, (row + 8) * PITCH + cb);
+          dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
+          const u32x2 qlo = lds_read_tr(qb, row * PITCH + cb);
+          const u32x2 qhi = lds_read_tr(qb, (row + 8) * PITCH + cb);
+          dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+        }
+      }
+
+    if (it + 1 < n_iter) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < a.Tk) {
+    uint16_t* dkp = a.dk + kvoff + (size_t)key * D;
+    uint16_t* dvp = a.dv + kvoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        const f32x16& kk = dk_acc[db];
+        const f32x16& vv = dv_acc[db];
+        *(u32x2*)(dkp + d0) = u32x2{pack_bf16x2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale),
+                                    pack_bf16x2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale)};
+        *(u32x2*)(dvp + d0) = u32x2{pack_bf16x2(vv[4 * g4], vv[4 * g4 + 1]),
+                                    pack_bf16x2(vv[4 * g4 + 2], vv[4 * g4 + 3])};
+      }
+  }
+}
+
+// -------------------------------------------------------------------- dq
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int PITCH = (D + 16) * 2;
+  constexpr int TILE = BC * PITCH;
+  constexpr int CH = D / 8;
+  constexpr int LOADS = BC * CH / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * 2 * TILE];
+  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt_lin = (int)(t % (uint32_t)n_qtiles);
+  const int bh = (int)(t / (uint32_t)n_qtiles);
+  const int qt = CAUSAL ? (n_qtiles - 1 - qt_lin) : qt_lin;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int q0 = qt * BR;
+  const size_t qoff = (size_t)bh * a.Tq;
+  const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
+  const uint16_t* __restrict__ Kp = a.k + kvoff;
+  const uint16_t* __restrict__ Vp = a.v + kvoff;
+
+  const int shift = a.Tk - a.Tq;
+  int kv_end = a.Tk;
+  if (CAUSAL) kv_end = min(a.Tk, q0 + BR + shift);
+  const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  const int qrow = q0 + wave * 32 + col;
+  const bool live = qrow < a.Tq;
+  bf16x8 qf[D / 16], gf[D / 16];
+  float lse2 = INFINITY, delta = 0.f;
+  {
+    const uint16_t* qs = a.q + (qoff + (live ? qrow : 0)) * D + 8 * half;
+    const uint16_t* gs = a.dout + (qoff + (live ? qrow : 0)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = as_bf16x8(live ? global_load_b128(qs + s * 16) : u32x4{0, 0, 0, 0});
+      gf[s] = as_bf16x8(live ? global_load_b128(gs + s * 16) : u32x4{0, 0, 0, 0});
+    }
+    if (live) {
+      const float l = a.lse[qoff + qrow];
+      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      delta = a.delta[qoff + qrow];
+    }
+  }
+
+  f32x16 dq_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
+
+  u32x4 kst[LOADS], vst[LOADS];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / CH, ch = c % CH;
+      const int kr = j * BC + row;
+      if (kr < a.Tk) {
+        kst[i] = global_load_b128(Kp + (size_t)kr * D + ch * 8);
+        vst[i] = global_load_b128(Vp + (size_t)kr * D + ch * 8);
+      } else {
+        kst[i] = u32x4{0, 0, 0, 0};
+        vst[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
+    FA_LDS uint8_t* vb = kb + TILE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / CH, ch = c % CH;
+      lds_write_b128(kb, row * PITCH + ch * 16, kst[i]);
+      lds_write_b128(vb, row * PITCH + ch * 16, vst[i]);
+    }
+  };
+
+  if (n_kv > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const int grp = lane >> 4, gi = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
+  const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
+
+  for (int j = 0; j < n_kv; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_kv) load_tile(j + 1);
+    const FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
+    const FA_LDS uint8_t* vb = kb + TILE;
+
+    f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+    for (int kb_i = 0; kb_i < BC / 32; ++kb_i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb_i][r] = 0.f;
+        dp[kb_i][r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int off = (kb_i * 32 + col) * PITCH + (ks * 16 + 8 * half) * 2;
+        s[kb_i] = mfma32(as_bf16x8(lds_read_b128(kb, off)), qf[ks], s[kb_i]);
+        dp[kb_i] = mfma32(as_bf16x8(lds_read_b128(vb, off)), gf[ks], dp[kb_i]);
+      }
+    }
+
+    const int key_base = j * BC;
+    const bool need_mask = (key_base + BC > a.Tk) ||
+                           (CAUSAL && key_base + BC - 1 > q0 + wave * 32 + shift);
+    uint32_t dsw[BC / 32][8];
+#pragma unroll
+    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = exp2_fast(fmaf(s[kb_i][r], a.c, -lse2));
+        float p1 = exp2_fast(fmaf(s[kb_i][r + 1], a.c, -lse2));
+        if (need_mask) {
+          const int kr = key_base + kb_i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (kr > lim) p0 = 0.f;
+          if (kr + 1 > lim) p1 = 0.f;
+        }
+        dsw[kb_i][r >> 1] = pack_bf16x2(p0 * (dp[kb_i][r] - delta), p1 * (dp[kb_i][r + 1] - delta));
+      }
+
+    // dQ^T[d, query] += K^T[d, key] dS^T[key, query]
+#pragma unroll
+    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 sb = as_bf16x8(u32x4{dsw[kb_i][4 * hs], dsw[kb_i][4 * hs + 1],
+                                          dsw[kb_i][4 * hs + 2], dsw[kb_i][4 * hs + 3]});
+        const int row = kb_i * 32 + hs * 16 + tr_row;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int cb = (db * 32 + tr_col) * 2;
+          const u32x2 lo = lds_read_tr(kb, row * PITCH + cb);
+          const u32x2 hi = lds_read_tr(kb, (row + 8) * PITCH + cb);
+          dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
+        }
+      }
+
+    if (j + 1 < n_kv) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (live) {
+    uint16_t* dst = a.dq + (qoff + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        const f32x16& q = dq_acc[db];
+        *(u32x2*)(dst + d0) = u32x2{pack_bf16x2(q[4 * g4] * a.scale, q[4 * g4 + 1] * a.scale),
+                                    pack_bf16x2(q[4 * g4 + 2] * a.scale, q[4 * g4 + 3] * a.scale)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int D, bool CAUSAL>
+static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  const long long n_rows = (long long)a.B * a.Hq * a.Tq;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((n_rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     a, n_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_ktiles = (a.Tk + 127) / 128;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(256), 0, stream,
+                     a, n_ktiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qtiles = (a.Tq + 127) / 128;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(256), 0, stream,
+                     a, n_qtiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+}
+
+}  // namespace fa

@@ -146,6 +146,38 @@ def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: in
     return scale * (ds @ kk)
 
 
+def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk: int, keys):
+    """dK and dV for some keys of one (batch, KV head).
+
+    A key's gradient sums contributions of every query row of the group that
+    sees it; each row's probabilities still come from that row's whole score
+    row. Keys near the end of a causal sequence are seen by few rows, so they
+    can be evaluated at any length. Returns (dK [n,d], dV [n,d]) in fp64."""
+    Hq, Hkv = np.shape(q)[1], np.shape(k)[1]
+    g = Hq // Hkv
+    Tq = np.shape(q)[2]
+    kk = np.asarray(k[b, hk], dtype=np.float64)
+    vv = np.asarray(v[b, hk], dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.int64)
+    Tk = kk.shape[0]
+    first = 0
+    if causal:
+        first = max(0, int(keys.min()) - (Tk - Tq))
+    dk = np.zeros((keys.shape[0], kk.shape[1]))
+    dv = np.zeros((keys.shape[0], vv.shape[1]))
+    for h in range(hk * g, (hk + 1) * g):
+        qq = np.asarray(q[b, h], dtype=np.float64)
+        gg = np.asarray(do[b, h], dtype=np.float64)
+        for s in range(first, Tq, _ROW_BLOCK):
+            r = np.arange(s, min(Tq, s + _ROW_BLOCK))
+            p, _ = row_probs(qq[r], kk, scale, r, Tq, causal)
+            dp = gg[r] @ vv.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dv += p[:, keys].T @ gg[r]
+            dk += scale * (ds[:, keys].T @ qq[r])
+    return dk, dv
+
+
 def decode(q, k_cache, v_cache, seq_lens, scale: float, heads=None):
     """One query token per (batch, head) against the first seq_lens[b] cached keys.
 

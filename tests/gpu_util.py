@@ -4,9 +4,11 @@ the tolerance rules the HIP path must meet against the fp64 oracle.
 Tolerances (written here, used by every GPU test):
   * fp32 path: max |x - ref| <= 1e-5, taken relative to max(1, |ref|) so that
     the pages' worked rows (|O| ~ 62) get the same ~2-3 fp32 ulps;
-  * bf16 path: max |x - ref| <= 2e-2 and ||x - ref||_2 / ||ref||_2 <= 1e-2 for
-    every output tensor (the relative term keeps the check meaningful when
-    |O| ~ sqrt(e/T) is small);
+  * bf16 path: max |x - ref| / max(1, |ref|) <= 2e-2 and
+    ||x - ref||_2 / ||ref||_2 <= 1e-2 for every output tensor. The relative
+    L2 term keeps the check meaningful when |O| ~ sqrt(e/T) is small; the
+    max(1, |ref|) divisor only matters for outputs above 1 in magnitude, where
+    storing the exact answer in bf16 alone can miss by more than 2e-2;
   * LSE: max |x - ref| <= 1e-4 (bf16 inputs), <= 1e-5 (fp32 inputs).
 """
 from __future__ import annotations
@@ -36,14 +38,21 @@ def report(name: str, got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
     max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
     den = float(np.linalg.norm(np.where(fin, ref, 0)))
     rel = float(np.linalg.norm(diff) / den) if den > 0 else max_abs
-    print(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    refv = np.where(fin, ref, 0.0)
+    floor = float(np.max(np.abs(inputs.bf16_bits_to_f32(inputs.bf16_bits_from_f32(refv.astype(np.float32)))
+                                - refv))) if refv.size else 0.0
+    print(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} max|ref|={float(np.max(np.abs(refv), initial=0)):.3e} "
+          f"bf16_floor={floor:.3e}", flush=True)
     return max_abs, rel
 
 
 def check_bf16(name: str, got, ref) -> None:
     got = host(got) if isinstance(got, torch.Tensor) else got
     max_abs, rel = report(name, got, ref)
-    assert max_abs <= 2e-2 and rel <= 1e-2, f"{name}: max_abs={max_abs:.3e} rel={rel:.3e}"
+    fin = np.isfinite(ref)
+    refv = np.where(fin, ref, 0.0)
+    scaled = float(np.max(np.abs(np.where(fin, got, 0.0) - refv) / np.maximum(1.0, np.abs(refv)), initial=0.0))
+    assert scaled <= 2e-2 and rel <= 1e-2, f"{name}: max_abs={max_abs:.3e} (scaled {scaled:.3e}) rel={rel:.3e}"
 
 
 def check_f32(name: str, got, ref) -> None:

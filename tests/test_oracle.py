@@ -169,6 +169,20 @@ def test_backward_dq_rows_match_full():
     assert np.allclose(dq_r, dq[0, 3, rows], atol=1e-14)
 
 
+def test_backward_sampled_keys_match_full():
+    rng = np.random.Generator(np.random.PCG64(15))
+    q = rng.standard_normal((2, 4, 37, 5))
+    k = rng.standard_normal((2, 2, 41, 5))
+    v = rng.standard_normal((2, 2, 41, 5))
+    do = rng.standard_normal((2, 4, 37, 5))
+    for causal in (False, True):
+        _, dk, dv = ref.attention_bwd(q, k, v, do, 0.6, causal)
+        keys = np.array([40, 3, 22])
+        dk_s, dv_s = ref.attention_bwd_dkdv_keys(q, k, v, do, 0.6, causal, 1, 1, keys)
+        assert np.allclose(dk_s, dk[1, 1, keys], atol=1e-13)
+        assert np.allclose(dv_s, dv[1, 1, keys], atol=1e-13)
+
+
 def test_backward_sum_identities():
     """sum_j dV_j equals the summed dO of the group (rows of P sum to one) and
     sum_j dK_j is zero (each row of dS sums to zero)."""
