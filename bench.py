@@ -36,6 +36,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 
+COPY_BYTES = 1 << 30          # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
+
 METRIC = "attention fwd/bwd TFLOPS and % of MI355X bf16 MFMA peak; decode HBM GB/s"
 
 WORKLOADS = {
@@ -213,8 +215,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the side measurements")
-    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "decode"],
-                    help="run one measurement alone (profiling runs)")
+    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "decode", "copy"],
+                    help="run one measurement alone (profiling runs); 'copy' runs a plain device copy "
+                         "of 1 GiB, the calibration for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -236,6 +239,18 @@ def main():
     if args.only == "decode":
         print(json.dumps(run_decode(args.steps, args.warmup)), flush=True)
         return 0
+    if args.only == "copy":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": max(1, args.steps)}), flush=True)
+        return 0
+    if args.only == "step":
+        args.no_extras = True
+        args.no_cpu_baseline = True
 
     backward = not args.workload.endswith("-fwd")
     res = run_attention(args.workload, args.steps, args.warmup, backward=backward)

@@ -29,7 +29,9 @@
  *     "query i sees keys 0..i" rule when Tq == Tk. A query that sees no key
  *     (only possible when causal and Tq > Tk) gets O = 0 and LSE = -inf.
  *   - scale multiplies Q K^T and must be finite and > 0 (typically 1/sqrt(d)).
- *   - d must be 64 or 128. Every pointer must be 16-byte aligned.
+ *   - d must be 64 or 128. Every pointer must be 16-byte aligned. One head's
+ *     rows must span less than 2^31 bytes (T * d * 2 < 2^31, i.e. T below 8M at
+ *     d = 128): kernels address them with 32-bit offsets.
  *   - Every call is asynchronous on `stream` (0 = the null stream); results
  *     are valid once the stream has completed. The library never allocates,
  *     frees or synchronises, and keeps no global mutable state: concurrent

@@ -21,6 +21,8 @@ int check_common(int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale) {
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // element offsets are formed in size_t, row indices in int
   if ((int64_t)B * Hq > INT32_MAX / 2 || (int64_t)B * Hkv > INT32_MAX / 2) return FA_ERR_INVALID_ARG;
+  // one head's rows are addressed with 32-bit buffer offsets
+  if ((int64_t)Tq * d * 2 >= fa::kMaxHeadBytes || (int64_t)Tk * d * 2 >= fa::kMaxHeadBytes) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
@@ -51,7 +53,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
-  if ((int64_t)((Tq + 127) / 128) * B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  const int br = fa::fwd_rows_per_workgroup(d);
+  if ((int64_t)((Tq + br - 1) / br) * B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

@@ -85,6 +85,16 @@ __device__ __forceinline__ u32x4 global_load_b128(const void* p) {
   return *(const u32x4*)p;
 }
 
+// Raw buffer resource over [p, p + bytes): loads at byte offsets >= bytes
+// return zeros without touching memory, which keeps tile loads branch free.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset that is always out of range
+
 // Workgroup index remap so that consecutive logical tiles share one XCD.
 // Hardware deals workgroups round-robin over the 8 XCDs (id % 8); logical
 // tile t is placed on XCD t / ceil-share, which keeps the tiles of one head

@@ -5,45 +5,73 @@
 // an Obstacle"; aimlrounds "FlashAttention", "Softmax without seeing the
 // whole row"): a tile of queries stays on chip while key/value tiles stream
 // past it; each query row keeps a running maximum m, a running sum l of
-// exponentials relative to m, and a running weighted sum u; when a tile
-// raises the maximum to m', l and u are both scaled by e^(m - m') before the
-// tile's own terms are added. Scores and probabilities live only in
-// registers.
+// exponentials relative to m, and a running weighted sum u; when the maximum
+// moves to m', l and u are both scaled by e^(m - m') before the tile's own
+// terms are added. Scores and probabilities live only in registers.
 //
 // gfx950 mapping
-//   * workgroup = 4 waves = 128 query rows (32 per wave); grid = query tiles
-//     x heads x batch, remapped so the tiles of one head share an XCD (and
-//     its L2), causal tiles longest first.
-//   * K and V tiles of 64 keys stream HBM -> registers -> LDS, double
-//     buffered (one barrier per tile). Rows are padded by 32 bytes so that
-//     both the row reads of K and the transposed reads of V are free of
-//     bank conflicts.
+//   * workgroup = NW waves x 32 query rows (NW = 8 at d = 128, 4 at d = 64);
+//     grid = query tiles x heads x batch, remapped so that the tiles of one
+//     head share an XCD (and its L2), causal tiles longest first.
+//   * 64-key K and V tiles stream HBM -> registers -> LDS through buffer
+//     loads (out-of-range rows read as zeros, so the loop has no branches),
+//     double buffered with one barrier per tile. Row pitches are chosen for
+//     the 64-bank LDS: K rows are padded by 16 bytes (the 16 lanes of a
+//     128-bit row read land on distinct banks), V rows by 64 bytes (the
+//     transposed 64-bit reads land on distinct banks).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query
-//     column and 16 keys, so the row maximum is an in-lane max plus one
-//     permlane32 swap, and the running sum stays a per-lane partial until
-//     the end.
+//     column and 16 keys of a 32-key block, so the row maximum is an in-lane
+//     max plus one permlane32 swap and the running sum stays a per-lane
+//     partial until the end.
 //   * O^T = V^T P^T: the probabilities are reused straight from the S^T
-//     accumulator layout as the B operand (the contraction order over keys
-//     is permuted identically on the A side), V^T comes from
-//     ds_read_b64_tr_b16; every O^T register of a lane belongs to that
-//     lane's query, so the e^(m - m') rescale is a per-lane scalar.
+//     accumulator layout as the B operand, V^T comes from ds_read_b64_tr_b16,
+//     and every O^T register of a lane belongs to that lane's query.
+//   * Software pipeline: while the vector unit turns S_j into probabilities
+//     and feeds them to the PV products, the matrix cores already compute
+//     S_{j+1} from the next K tile.
+//   * The running maximum is only moved when some row of the wave grows by
+//     more than 2^8; otherwise the stale maximum is kept, the probabilities
+//     stay below 256 and l and u need no rescale (the result is the same up
+//     to rounding, since l and u always share one reference).
 //   * exponentials are exp2 with scale*log2(e) folded into one FMA.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_internal.h"
 
 namespace fa {
 
+namespace {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int NW = D == 128 ? 8 : 4;   // waves per workgroup
+  static constexpr int BR = 32 * NW;            // query rows per workgroup
+  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int NT = 64 * NW;            // threads per workgroup
+  static constexpr int KPITCH = (D + 8) * 2;    // LDS bytes per K row
+  static constexpr int VPITCH = (D + 32) * 2;   // LDS bytes per V row
+  static constexpr int KTILE = BC * KPITCH;
+  static constexpr int VTILE = BC * VPITCH;
+  static constexpr int CH = D / 8;              // 16-byte chunks per row
+  static constexpr int LOADS = BC * CH / NT;    // chunks per thread per tile
+  static_assert(LOADS >= 1 && LOADS * NT == BC * CH, "a tile must split evenly over the workgroup");
+};
+
+// Stale-maximum allowance (log2 units): probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
+}  // namespace
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int BR = 128;                 // query rows per workgroup
-  constexpr int BC = 64;                  // keys per tile
-  constexpr int PITCH = (D + 16) * 2;     // LDS bytes per key row
-  constexpr int TILE = BC * PITCH;        // LDS bytes per K (or V) tile
-  constexpr int CH = D / 8;               // 16-byte chunks per key row
-  constexpr int LOADS = BC * CH / 256;    // chunks per thread per tensor
-  static_assert(LOADS * 256 == BC * CH, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * 2 * TILE];
-  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+__global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  constexpr int BR = C::BR, BC = C::BC, NT = C::NT, CH = C::CH, LOADS = C::LOADS;
+  constexpr int KPITCH = C::KPITCH, VPITCH = C::VPITCH, KTILE = C::KTILE, VTILE = C::VTILE;
+  constexpr int KB = BC / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * KTILE + 2 * VTILE];
+  FA_LDS uint8_t* kbuf = (FA_LDS uint8_t*)smem_raw;
+  FA_LDS uint8_t* vbuf = kbuf + 2 * KTILE;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5;             // which 16-key half of a 32-key block
@@ -58,25 +86,27 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int q0 = qt * BR;
   const size_t qoff = (size_t)bh * a.Tq * D;
   const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
-  const uint16_t* __restrict__ Kp = a.k + kvoff;
-  const uint16_t* __restrict__ Vp = a.v + kvoff;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
 
   // Causal: key j is visible to row i iff j <= i + shift.
   const int shift = a.Tk - a.Tq;
   int kv_end = a.Tk;
   if (CAUSAL) kv_end = min(a.Tk, q0 + BR + shift);
   const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  // Tiles [0, n_full) are complete and visible to every row of the workgroup.
+  int n_full = a.Tk / BC;
+  if (CAUSAL) n_full = min(n_full, max(0, q0 + shift + 1) / BC);
+  n_full = min(n_full, n_kv - 1);
 
-  // Q fragments: B operand of S^T = K Q^T (lane: query col, 8 dims).
+  // Q fragments: B operand of S^T = K Q^T (lane: query column, 8 dims).
   const int qrow = q0 + wave * 32 + col;
   bf16x8 qf[D / 16];
-  if (qrow < a.Tq) {
-    const uint16_t* src = a.q + qoff + (size_t)qrow * D + 8 * half;
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff, (uint32_t)a.Tq * D * 2);
+    const uint32_t base = qrow < a.Tq ? (uint32_t)(qrow * D + 8 * half) * 2 : kOutOfRange;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(global_load_b128(src + ks * 16));
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(buf_load_b128(qrs, base + ks * 32));
   }
 
   f32x16 oacc[D / 32];
@@ -87,128 +117,155 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   float m = -INFINITY;   // running max of scaled scores, log2 units
   float l = 0.f;         // this lane's partial running sum
 
-  u32x4 kst[LOADS], vst[LOADS];
-  auto load_tile = [&](int j) {
+  // This thread's share of a tile: LOADS 16-byte chunks (row, chunk).
+  uint32_t g_off[LOADS], k_lds[LOADS], v_lds[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / CH, ch = c % CH;
-      const int key = j * BC + row;
-      if (key < a.Tk) {
-        kst[i] = global_load_b128(Kp + (size_t)key * D + ch * 8);
-        vst[i] = global_load_b128(Vp + (size_t)key * D + ch * 8);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
+  for (int i = 0; i < LOADS; ++i) {
+    const int c = i * NT + tid;
+    const int row = c / CH, ch = c % CH;
+    g_off[i] = (uint32_t)(row * D + ch * 8) * 2;
+    k_lds[i] = row * KPITCH + ch * 16;
+    v_lds[i] = row * VPITCH + ch * 16;
+  }
+  u32x4 kst[LOADS], vst[LOADS];
+  auto tile_base = [&](int j) -> uint32_t { return j < n_kv ? (uint32_t)(j * BC * D * 2) : kOutOfRange; };
+  auto load_k = [&](int j) {
+    const uint32_t tb = tile_base(j);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) kst[i] = buf_load_b128(krs, tb + g_off[i]);
+  };
+  auto load_v = [&](int j) {
+    const uint32_t tb = tile_base(j);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) vst[i] = buf_load_b128(vrs, tb + g_off[i]);
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) lds_write_b128(kbuf + buf * KTILE, k_lds[i], kst[i]);
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) lds_write_b128(vbuf + buf * VTILE, v_lds[i], vst[i]);
+  };
+
+  // S^T[key, query] for the BC keys of the tile in `buf` and this wave's 32 queries.
+  const uint32_t k_rd = col * KPITCH + 16 * half;
+  auto scores = [&](int buf, f32x16* s) {
+    const FA_LDS uint8_t* kb = kbuf + buf * KTILE + k_rd;
+#pragma unroll
+    for (int kb_i = 0; kb_i < KB; ++kb_i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb_i][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 kv = lds_read_b128(kb, kb_i * 32 * KPITCH + ks * 32);
+        s[kb_i] = mfma32(as_bf16x8(kv), qf[ks], s[kb_i]);
       }
     }
   };
-  auto store_tile = [&](int buf) {
-    FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
-    FA_LDS uint8_t* vb = kb + TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / CH, ch = c % CH;
-      lds_write_b128(kb, row * PITCH + ch * 16, kst[i]);
-      lds_write_b128(vb, row * PITCH + ch * 16, vst[i]);
-    }
-  };
-
-  if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
 
   // Transposed-read coordinates of this lane inside its 16-lane group.
   const int grp = lane >> 4, gi = lane & 15;
   const int tr_row = 4 * (grp >> 1) + (gi >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
+  const uint32_t v_rd = tr_row * VPITCH + tr_col * 2;
 
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_kv) load_tile(j + 1);
-    const FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
-    const FA_LDS uint8_t* vb = kb + TILE;
+  // LDS ring: iteration j reads K_{j+1} from kbuf[(j+1)&1] and V_j from
+  // vbuf[j&1]; it refills kbuf[j&1] with K_{j+2} and vbuf[(j+1)&1] with V_{j+1}.
+  f32x16 s_a[KB], s_b[KB];
+  if (n_kv > 0) {
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    load_k(1);
+    store_k(1);
+    __syncthreads();
+    scores(0, s_a);
+    __syncthreads();   // every wave has read K_0 before K_2 replaces it
+  }
 
-    // S^T[key, query] for 64 keys x 32 queries.
-    f32x16 s[BC / 32];
-#pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb_i][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kv = lds_read_b128(kb, (kb_i * 32 + col) * PITCH + (ks * 16 + 8 * half) * 2);
-        s[kb_i] = mfma32(as_bf16x8(kv), qf[ks], s[kb_i]);
-      }
-    }
-
-    const int key_base = j * BC;
-    const bool need_mask = (key_base + BC > a.Tk) ||
-                           (CAUSAL && key_base + BC - 1 > q0 + wave * 32 + shift);
-    if (need_mask) {
+  // One tile: softmax of s_cur (S_j) and u += P V_j, with S_{j+1} -> s_nxt.
+  auto body = [&](int j, auto masked, auto has_next, f32x16* s_cur, f32x16* s_nxt) {
+    load_k(j + 2);
+    load_v(j + 1);
+    if constexpr (decltype(masked)::value) {
+      const int key_base = j * BC;
       const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
 #pragma unroll
-      for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+      for (int kb_i = 0; kb_i < KB; ++kb_i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key_base + kb_i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > lim) s[kb_i][r] = -INFINITY;
+          if (key > lim) s_cur[kb_i][r] = -INFINITY;
         }
     }
-
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+    for (int kb_i = 0; kb_i < KB; ++kb_i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb_i][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb_i][r]);
     mx = pair_max32(mx);
     const float m_new = fmaxf(m, mx * a.c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_use);
-    m = m_new;
-    l *= alpha;
+    if (__builtin_amdgcn_ballot_w64(m_new > m + kRescaleSlack)) {
+      // move the reference: l and u are rescaled together
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_ref);
+      l *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m = m_new;
+    }
+    const float m_ref = (m == -INFINITY) ? 0.f : m;
+    if constexpr (decltype(has_next)::value) scores((j + 1) & 1, s_nxt);
 
-    // P = 2^(S*c - m), packed to bf16 in the accumulator order.
-    uint32_t pw[BC / 32][8];
+    // P = 2^(S*c - m), 16 keys at a time, each block feeding its PV products.
+    const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
     float lsum = 0.f;
 #pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_fast(fmaf(s[kb_i][r], a.c, -m_use));
-        const float p1 = exp2_fast(fmaf(s[kb_i][r + 1], a.c, -m_use));
-        lsum += p0 + p1;
-        pw[kb_i][r >> 1] = pack_bf16x2(p0, p1);
-      }
-    l += lsum;
-
-    // O^T[d, query] += V^T[d, key] P^T[key, query], 16 keys per step.
-#pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+    for (int kb_i = 0; kb_i < KB; ++kb_i)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 pb = as_bf16x8(u32x4{pw[kb_i][4 * hs], pw[kb_i][4 * hs + 1],
-                                          pw[kb_i][4 * hs + 2], pw[kb_i][4 * hs + 3]});
-        const int row = kb_i * 32 + hs * 16 + tr_row;
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * hs + 2 * e;
+          const float p0 = exp2_fast(fmaf(s_cur[kb_i][r], a.c, -m_ref));
+          const float p1 = exp2_fast(fmaf(s_cur[kb_i][r + 1], a.c, -m_ref));
+          lsum += p0 + p1;
+          pw[e] = pack_bf16x2(p0, p1);
+        }
+        const bf16x8 pb = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+        const int row = kb_i * 32 + hs * 16;
+        // O^T[d, query] += V^T[d, key] P^T[key, query] for these 16 keys
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int cb = (db * 32 + tr_col) * 2;
-          const u32x2 lo = lds_read_tr(vb, row * PITCH + cb);
-          const u32x2 hi = lds_read_tr(vb, (row + 8) * PITCH + cb);
+          const u32x2 lo = lds_read_tr(vb, row * VPITCH + db * 64);
+          const u32x2 hi = lds_read_tr(vb, (row + 8) * VPITCH + db * 64);
           oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, oacc[db]);
         }
       }
+    l += lsum;
+    if constexpr (decltype(has_next)::value) {
+      store_k(j & 1);
+      store_v((j + 1) & 1);
+      __syncthreads();
+    }
+  };
 
-    if (j + 1 < n_kv) store_tile(buf ^ 1);
-    __syncthreads();
+  int j = 0;
+  for (; j + 2 <= n_full; j += 2) {   // unrolled by two: the score registers swap roles
+    body(j, std::false_type{}, std::true_type{}, s_a, s_b);
+    body(j + 1, std::false_type{}, std::true_type{}, s_b, s_a);
   }
+  for (; j < n_kv - 1; ++j) {
+    body(j, std::true_type{}, std::true_type{}, s_a, s_b);
+#pragma unroll
+    for (int kb_i = 0; kb_i < KB; ++kb_i) s_a[kb_i] = s_b[kb_i];
+  }
+  if (n_kv > 0) body(n_kv - 1, std::true_type{}, std::false_type{}, s_a, s_b);
 
   const float l_tot = pair_sum32(l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -229,14 +286,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 }
 
 template <int D, bool CAUSAL>
-static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+static hipError_t launch_fwd(FwdArgs a, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  a.n_qtiles = (a.Tq + C::BR - 1) / C::BR;
   const uint32_t n = (uint32_t)a.n_qtiles * (uint32_t)(a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
+int fwd_rows_per_workgroup(int d) { return d == 128 ? FwdCfg<128>::BR : FwdCfg<64>::BR; }
+
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
-  a.n_qtiles = (a.Tq + 127) / 128;
   if (d == 64) return causal ? launch_fwd<64, true>(a, stream) : launch_fwd<64, false>(a, stream);
   return causal ? launch_fwd<128, true>(a, stream) : launch_fwd<128, false>(a, stream);
 }

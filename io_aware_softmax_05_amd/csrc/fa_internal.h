@@ -62,9 +62,13 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
+int fwd_rows_per_workgroup(int d);
 hipError_t launch_fwd_f32(FwdF32Args a, int d, bool causal, hipStream_t stream);
 hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream);
+
+// Kernels address one head's rows through 32-bit buffer offsets below 2^31.
+constexpr long long kMaxHeadBytes = 1ll << 31;
 
 constexpr float kLog2eHost = 1.44269504088896340736f;
 constexpr int kDecodeMinChunk = 64;

@@ -65,6 +65,8 @@ def _fwd(**kw):
     (dict(q=MIS), fa.FA_ERR_INVALID_ARG),
     (dict(o=MIS), fa.FA_ERR_INVALID_ARG),
     (dict(lse=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(Tk=1 << 23, d=128), fa.FA_ERR_INVALID_ARG),   # one head's keys span 2^31 bytes
+    (dict(Tq=1 << 23, Tk=8, d=128), fa.FA_ERR_INVALID_ARG),
 ])
 def test_fwd_rejects(kw, want):
     assert _fwd(**kw) == want
