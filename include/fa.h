@@ -88,9 +88,10 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                hipStream_t stream);
 
 /*
- * Workspace bytes fa_bwd needs: one fp32 per query row for
- * D_i = sum_c dO_ic O_ic, rounded up to 256 bytes. Linear in Tq, never
- * quadratic (aimlrounds "FlashAttention": the N x N matrix is not stored).
+ * Workspace bytes fa_bwd needs: two fp32 per query row, the row's LSE in
+ * base-2 units and D_i = sum_c dO_ic O_ic, rounded up to 256 bytes. Linear in
+ * Tq, never quadratic (aimlrounds "FlashAttention": the N x N matrix is not
+ * stored).
  * Returns 0 for non-positive sizes.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d);

@@ -88,7 +88,7 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d) {
   if (B <= 0 || Hq <= 0 || Tq <= 0 || d <= 0) return 0;
-  return round256((size_t)B * Hq * Tq * sizeof(float));
+  return round256((size_t)B * Hq * Tq * 2 * sizeof(float));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -113,7 +113,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  a.delta = static_cast<float*>(workspace);
+  a.stats = static_cast<float*>(workspace);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.scale = scale;
   a.c = scale * fa::kLog2eHost;

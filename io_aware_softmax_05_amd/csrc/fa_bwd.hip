@@ -19,6 +19,8 @@
 //   dq    one workgroup per 128 query rows, laid out like the forward
 //         (S^T = K Q^T, one query per lane): dQ^T = K^T dS^T with K^T from
 //         transposed LDS reads.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_internal.h"
 
@@ -26,6 +28,8 @@ namespace fa {
 
 // ------------------------------------------------------------------ pre
 
+// Per query row: stats = (LSE * log2(e), D) with D = sum_c dO_c O_c; a row
+// that saw no key (LSE = -inf) gets +inf, so every rebuilt probability is 0.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long n_rows) {
   constexpr int LPR = D / 8;                   // lanes per row (16 B each)
@@ -45,26 +49,55 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long n_row
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < n_rows && part == 0) a.delta[row] = acc;
+  if (row < n_rows && part == 0) {
+    const float l = a.lse[row];
+    *(float2*)(a.stats + 2 * row) = float2{l == -INFINITY ? INFINITY : l * kLog2e, acc};
+  }
 }
 
 // ----------------------------------------------------------------- dk dv
 
+namespace {
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int NW = D == 64 ? 8 : 4;         // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int BK = 32 * NW;                 // keys per workgroup (32 per wave)
+  static constexpr int BQ = 32;                      // query rows per tile
+  static constexpr int ROWB = 2 * D;                 // LDS bytes per row (swizzled, unpadded)
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int QTILE = BQ * ROWB;            // one Q (or dO) tile
+  static constexpr int STATS = BQ * 8;               // (lse2, D) per row
+  static constexpr int STAGE = 2 * QTILE + STATS;
+  static constexpr int NSTAGE = 3;
+  static constexpr int TILE_DMA = 2 * BQ * CH / 64;  // 128-bit wave loads per tile (Q and dO)
+  static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
+  static constexpr int VM_PER_TILE = DMA_PER_WAVE + 1;   // + the stats load
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
+};
+
+}  // namespace
+
+// One workgroup per BK keys of one KV head; each wave owns 32 keys, with its
+// K and V rows held as MFMA B operands. The workgroup walks every query tile
+// (32 rows) of every query head of the group that can see one of its keys:
+//   S = Q K^T, dP = dO V^T        (A operands: Q and dO rows from LDS)
+//   P = 2^(S c - lse2), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS  (A operands: transposed LDS reads)
+// S puts one key per lane, so P and dS feed the second pair of products
+// straight from the accumulator registers. Q, dO and the row statistics reach
+// LDS through direct-to-LDS loads, three stages deep (two tiles in flight
+// while one is consumed); tiles are stored unpadded with an XOR swizzle.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
-  constexpr int BK = 128;                 // keys per workgroup
-  constexpr int BQ = 64;                  // query rows per tile
-  constexpr int PITCH = (D + 16) * 2;
-  constexpr int TILE = BQ * PITCH;        // one of Q / dO
-  constexpr int STATS = 2 * BQ * 4;       // lse2 and delta
-  constexpr int BUF = 2 * TILE + STATS;
-  constexpr int CH = D / 8;
-  constexpr int LOADS = BQ * CH / 256;
-  static_assert(LOADS * 256 == BQ * CH, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * BUF];
+__global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+  using C = DkdvCfg<D>;
+  constexpr int BQ = C::BQ, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
@@ -72,21 +105,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) 
   const int bhk = (int)(t / (uint32_t)n_ktiles);
   const int b = bhk / a.Hkv, hk = bhk - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int k0 = kt * BK;
-  const int key = k0 + wave * 32 + col;           // this lane's key
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + wave * 32;                 // first key of this wave
+  const int key = kw0 + col;                      // this lane's key
   const int shift = a.Tk - a.Tq;
   const size_t kvoff = (size_t)bhk * a.Tk * D;
 
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T.
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
   bf16x8 kf[D / 16], vf[D / 16];
   {
-    const bool live = key < a.Tk;
-    const uint16_t* ks = a.k + kvoff + (size_t)(live ? key : 0) * D + 8 * half;
-    const uint16_t* vs = a.v + kvoff + (size_t)(live ? key : 0) * D + 8 * half;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+    const uint32_t base = key < a.Tk ? (uint32_t)(key * D + 8 * half) * 2 : kOutOfRange;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      kf[s] = as_bf16x8(live ? global_load_b128(ks + s * 16) : u32x4{0, 0, 0, 0});
-      vf[s] = as_bf16x8(live ? global_load_b128(vs + s * 16) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = as_bf16x8(buf_load_b128(krs, base + ks * 32));
+      vf[ks] = as_bf16x8(buf_load_b128(vrs, base + ks * 32));
     }
   }
 
@@ -99,145 +133,141 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) 
       dk_acc[db][r] = 0.f;
     }
 
-  // Query tiles that can see any key of this workgroup.
+  // Query tiles that can see any key of this workgroup, for each query head of the group.
   int qt_begin = 0;
   if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
   const int n_qt = (a.Tq + BQ - 1) / BQ;
   const int per_head = max(0, n_qt - qt_begin);
   const int n_iter = per_head * G;
 
-  u32x4 qst[LOADS], gst[LOADS];
-  float lse_st = 0.f, del_st = 0.f;
-  auto load_tile = [&](int it) {
-    const int hq = hk * G + it / per_head;
-    const int q0 = (qt_begin + it % per_head) * BQ;
-    const size_t qoff = ((size_t)b * a.Hq + hq) * a.Tq;
+  // This thread's share of the tile loads: physical chunk p of the tile holds
+  // logical chunk p ^ swz(row) of its row.
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_row[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  bool dma_is_do[C::DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / CH, ch = c % CH;
-      const int qr = q0 + row;
-      if (qr < a.Tq) {
-        qst[i] = global_load_b128(a.q + (qoff + qr) * D + ch * 8);
-        gst[i] = global_load_b128(a.dout + (qoff + qr) * D + ch * 8);
-      } else {
-        qst[i] = u32x4{0, 0, 0, 0};
-        gst[i] = u32x4{0, 0, 0, 0};
-      }
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int n = wave * C::DMA_PER_WAVE + i;
+    const int m = n % (C::TILE_DMA / 2);
+    dma_is_do[i] = n >= C::TILE_DMA / 2;
+    const int p = 64 * m + lane;
+    const int r = p / CH, pc = p % CH;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+    dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
+  }
+  const int st_row = lane >> 1;                   // stats load: (row, lse2 or D)
+
+  // Tile iterator for the loads (two tiles ahead of the compute).
+  int ld_it = 0, ld_h = 0, ld_qi = qt_begin;
+  auto issue = [&](int stage) {
+    FA_LDS uint8_t* st = smem + stage * STAGE;
+    const bool live = ld_it < n_iter;
+    const int q0 = ld_qi * BQ;
+    const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats + rows * 2, (uint32_t)a.Tq * 8);
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const bool ok = live && q0 + (int)dma_row[i] < a.Tq;
+      const uint32_t off = ok ? (uint32_t)q0 * D * 2 + dma_off[i] : kOutOfRange;
+      dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], off);
     }
-    if (tid < BQ) {
-      const int qr = q0 + tid;
-      if (qr < a.Tq) {
-        const float l = a.lse[qoff + qr];
-        // a row with no visible key (LSE = -inf) must give P = 0
-        lse_st = l == -INFINITY ? INFINITY : l * kLog2e;
-        del_st = a.delta[qoff + qr];
-      } else {
-        lse_st = INFINITY;
-        del_st = 0.f;
-      }
+    const bool sok = live && q0 + st_row < a.Tq;
+    dma_b32(srs, st + 2 * QTILE, sok ? (uint32_t)(q0 * 2 + lane) * 4 : kOutOfRange);
+    ++ld_it;
+    if (++ld_qi == n_qt) {
+      ld_qi = qt_begin;
+      ++ld_h;
     }
   };
-  auto store_tile = [&](int buf) {
-    FA_LDS uint8_t* qb = smem + buf * BUF;
-    FA_LDS uint8_t* gb = qb + TILE;
-    FA_LDS float* st = (FA_LDS float*)(gb + TILE);
+
+  // LDS read offsets (bytes inside a tile).
+  const uint32_t fq = swz<D>(col);
+  const uint32_t q_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
+  const int grp = lane >> 4, gi = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+  const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
+  const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
+  const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
+  const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
+
+  auto body = [&](const FA_LDS uint8_t* st, int q0, auto masked) {
+    const FA_LDS uint8_t* qt = st;
+    const FA_LDS uint8_t* gt = st + QTILE;
+    const FA_LDS uint8_t* stt = st + 2 * QTILE;
+    // S = Q K^T and dP = dO V^T for 32 queries x 32 keys (one key per lane).
+    f32x16 s, dp;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / CH, ch = c % CH;
-      lds_write_b128(qb, row * PITCH + ch * 16, qst[i]);
-      lds_write_b128(gb, row * PITCH + ch * 16, gst[i]);
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
     }
-    if (tid < BQ) {
-      st[tid] = lse_st;
-      st[BQ + tid] = del_st;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mfma32(as_bf16x8(lds_read_b128(qt, q_rd ^ (32 * ks))), kf[ks], s);
+      dp = mfma32(as_bf16x8(lds_read_b128(gt, q_rd ^ (32 * ks))), vf[ks], dp);
+    }
+    // P and dS, packed to bf16 in the accumulator order (rows 8 g4 + 4 half + e).
+    uint32_t pw[8], dsw[8];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int rq = 8 * g4 + 4 * half;
+      const f32x4 s01 = *(const FA_LDS f32x4*)(stt + rq * 8);
+      const f32x4 s23 = *(const FA_LDS f32x4*)(stt + rq * 8 + 16);
+      const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+      const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e;
+        float pe = exp2_fast(fmaf(s[r], a.c, -l2[e]));
+        if constexpr (decltype(masked)::value) {
+          if (key > q0 + rq + e + shift) pe = 0.f;
+        }
+        p[e] = pe;
+        ds[e] = pe * (dp[r] - dl[e]);
+      }
+      pw[2 * g4] = pack_bf16x2(p[0], p[1]);
+      pw[2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
+      dsw[2 * g4] = pack_bf16x2(ds[0], ds[1]);
+      dsw[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const bf16x8 pb = as_bf16x8(u32x4{pw[4 * hs], pw[4 * hs + 1], pw[4 * hs + 2], pw[4 * hs + 3]});
+      const bf16x8 sb = as_bf16x8(u32x4{dsw[4 * hs], dsw[4 * hs + 1], dsw[4 * hs + 2], dsw[4 * hs + 3]});
+      const uint32_t hb = hs * 16 * ROWB;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 glo = lds_read_tr(gt, hb + (tr_lo ^ (64 * db)));
+        const u32x2 ghi = lds_read_tr(gt, hb + (tr_hi ^ (64 * db)));
+        dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
+        const u32x2 qlo = lds_read_tr(qt, hb + (tr_lo ^ (64 * db)));
+        const u32x2 qhi = lds_read_tr(qt, hb + (tr_hi ^ (64 * db)));
+        dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+      }
     }
   };
 
   if (n_iter > 0) {
-    load_tile(0);
-    store_tile(0);
+    issue(0);
+    issue(1);
+    wait_vm_barrier<C::VM_PER_TILE>();   // K/V rows and tile 0 have landed
   }
-  __syncthreads();
-
-  const int grp = lane >> 4, gi = lane & 15;
-  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
-
+  int cur_stage = 0, ld_stage = 2, cur_qi = qt_begin;
   for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_iter) load_tile(it + 1);
-    const FA_LDS uint8_t* qb = smem + buf * BUF;
-    const FA_LDS uint8_t* gb = qb + TILE;
-    const FA_LDS float* st = (const FA_LDS float*)(gb + TILE);
-    const int q0 = (qt_begin + it % per_head) * BQ;
-
-    // S = Q K^T and dP = dO V^T for 64 queries x 32 keys (one key per lane).
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qblk = 0; qblk < 2; ++qblk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[qblk][r] = 0.f;
-        dp[qblk][r] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int off = (qblk * 32 + col) * PITCH + (ks * 16 + 8 * half) * 2;
-        s[qblk] = mfma32(as_bf16x8(lds_read_b128(qb, off)), kf[ks], s[qblk]);
-        dp[qblk] = mfma32(as_bf16x8(lds_read_b128(gb, off)), vf[ks], dp[qblk]);
-      }
-    }
-
-    const bool need_mask = CAUSAL && (q0 < k0 + wave * 32 + 31 - shift);
-    uint32_t pw[2][8], dsw[2][8];
-#pragma unroll
-    for (int qblk = 0; qblk < 2; ++qblk)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int rq = qblk * 32 + 8 * g4 + 4 * half;   // first of 4 consecutive rows
-        const f32x4 l2 = *(const FA_LDS f32x4*)(st + rq);
-        const f32x4 dl = *(const FA_LDS f32x4*)(st + BQ + rq);
-        float p[4], ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float pe = exp2_fast(fmaf(s[qblk][r], a.c, -l2[e]));
-          if (need_mask && key > q0 + rq + e + shift) pe = 0.f;
-          p[e] = pe;
-          ds[e] = pe * (dp[qblk][r] - dl[e]);
-        }
-        pw[qblk][2 * g4] = pack_bf16x2(p[0], p[1]);
-        pw[qblk][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
-        dsw[qblk][2 * g4] = pack_bf16x2(ds[0], ds[1]);
-        dsw[qblk][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
-      }
-
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
-#pragma unroll
-    for (int qblk = 0; qblk < 2; ++qblk)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 pb = as_bf16x8(u32x4{pw[qblk][4 * hs], pw[qblk][4 * hs + 1],
-                                          pw[qblk][4 * hs + 2], pw[qblk][4 * hs + 3]});
-        const bf16x8 sb = as_bf16x8(u32x4{dsw[qblk][4 * hs], dsw[qblk][4 * hs + 1],
-                                          dsw[qblk][4 * hs + 2], dsw[qblk][4 * hs + 3]});
-        const int row = qblk * 32 + hs * 16 + tr_row;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int cb = (db * 32 + tr_col) * 2;
-          const u32x2 glo = lds_read_tr(gb, row * PITCH + cb);
-          const u32x2 ghi = lds_read_tr(gb, (row + 8) * PITCH + cb);
-          dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
-          const u32x2 qlo = lds_read_tr(qb, row * PITCH + cb);
-          const u32x2 qhi = lds_read_tr(qb, (row + 8) * PITCH + cb);
-          dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
-        }
-      }
-
-    if (it + 1 < n_iter) store_tile(buf ^ 1);
-    __syncthreads();
+    issue(ld_stage);                      // tile it+2 (zeros past the end)
+    const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
+    const int q0 = cur_qi * BQ;
+    // some (row, key) pair of this wave is masked
+    if (CAUSAL && q0 + shift < kw0 + 31) body(st, q0, std::true_type{});
+    else body(st, q0, std::false_type{});
+    wait_vm_barrier<C::VM_PER_TILE>();    // tile it+1 has landed; this stage is free
+    cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
+    ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
+    if (++cur_qi == n_qt) cur_qi = qt_begin;
   }
 
   if (key < a.Tk) {
@@ -303,9 +333,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
       gf[s] = as_bf16x8(live ? global_load_b128(gs + s * 16) : u32x4{0, 0, 0, 0});
     }
     if (live) {
-      const float l = a.lse[qoff + qrow];
-      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-      delta = a.delta[qoff + qrow];
+      const float2 st = *(const float2*)(a.stats + 2 * (qoff + qrow));
+      lse2 = st.x;
+      delta = st.y;
     }
   }
 
@@ -439,8 +469,8 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
                      a, n_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_ktiles = (a.Tk + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(256), 0, stream,
+  const int n_ktiles = (a.Tk + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(DkdvCfg<D>::NT), 0, stream,
                      a, n_ktiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -95,6 +95,42 @@ __device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset that is always out of range
 
+// Direct global -> LDS loads (no registers): lane l of the wave writes its
+// 16 (or 4) bytes to lds_wave_base + 16 l (or 4 l); the global offset is per lane.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t r, FA_LDS void* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t r, FA_LDS void* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 4, off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight and
+// its LDS operations are done, then meet the workgroup barrier. The asm has a
+// memory clobber, so the compiler keeps LDS accesses on their side of it; the
+// wait is what makes earlier direct-to-LDS loads visible to the other waves.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// XOR swizzle of the 16-byte chunks of a row of D bf16 values, for LDS tiles
+// stored without padding. Chunk c of row r lives at chunk c ^ swz<D>(r).
+// With 64 four-byte banks it makes both access patterns conflict free:
+//   * 128-bit reads of one chunk from 16 consecutive rows (MFMA A operand);
+//   * 64-bit transposed reads of 4 consecutive rows x 64 bytes (two 16-lane
+//     groups of ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ uint32_t swz(uint32_t r) {
+  static_assert(D == 64 || D == 128, "head width");
+  if constexpr (D == 128) {
+    return ((r & 3u) << 2) | ((r >> 2) & 3u);
+  } else {
+    const uint32_t k = (r >> 1) & 7u;   // two 128-byte rows share a bank row
+    return ((k & 1u) << 2) | ((k >> 1) & 3u);
+  }
+}
+
 // Workgroup index remap so that consecutive logical tiles share one XCD.
 // Hardware deals workgroups round-robin over the 8 XCDs (id % 8); logical
 // tile t is placed on XCD t / ceil-share, which keeps the tiles of one head

@@ -55,7 +55,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;             // [B,Hq,Tq] workspace: rowsum(dO * O)
+  float* stats;             // [B,Hq,Tq,2] workspace: (LSE * log2 e, rowsum(dO * O))
   int B, Hq, Hkv, Tq, Tk;
   float scale;
   float c;                  // scale * log2(e)

@@ -79,7 +79,7 @@ def test_fwd_rejects(kw, want):
 
 
 def test_workspace_sizes_are_linear():
-    assert fa.fa_bwd_workspace_size(1, 32, 32768, 128) == 32 * 32768 * 4          # 4 MiB, one fp32 per row
+    assert fa.fa_bwd_workspace_size(1, 32, 32768, 128) == 32 * 32768 * 8          # 8 MiB, two fp32 per row
     assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
     w1 = fa.fa_decode_workspace_size(16, 32, 32768, 128)
     w2 = fa.fa_decode_workspace_size(16, 32, 65536, 128)
