@@ -290,17 +290,45 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
 
 // -------------------------------------------------------------------- dq
 
+namespace {
+
+template <int D>
+struct DqCfg {
+  static constexpr int NW = 8;                        // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;                  // query rows per workgroup
+  static constexpr int BC = D == 64 ? 64 : 32;        // keys per tile
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CH = D / 8;
+  static constexpr int KTILE = BC * ROWB;             // one K (or V) tile
+  static constexpr int STAGE = 2 * KTILE;
+  static constexpr int NSTAGE = 3;
+  static constexpr int TILE_DMA = 2 * BC * CH / 64;   // 128-bit wave loads per tile (K and V)
+  static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
+};
+
+}  // namespace
+
+// One workgroup per BR query rows; each wave owns 32 rows, with its Q and dO
+// rows held as MFMA B operands, and walks the key tiles its rows can see:
+//   S^T = K Q^T, dP^T = V dO^T        (A operands: K and V rows from LDS)
+//   P = 2^(S c - lse2), dS = P (dP - D)
+//   dQ^T += K^T dS^T                   (A operand: transposed reads of K)
+// The layout mirrors the forward kernel: one query per lane, so dS^T feeds
+// the last product from the accumulator registers. K and V arrive through
+// direct-to-LDS loads, three stages deep, swizzled like the dK/dV kernel's
+// tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
-  constexpr int BR = 128, BC = 64;
-  constexpr int PITCH = (D + 16) * 2;
-  constexpr int TILE = BC * PITCH;
-  constexpr int CH = D / 8;
-  constexpr int LOADS = BC * CH / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * 2 * TILE];
+__global__ __launch_bounds__(DqCfg<D>::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  using C = DqCfg<D>;
+  constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
+  constexpr int KB = BC / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
@@ -309,34 +337,33 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   const int qt = CAUSAL ? (n_qtiles - 1 - qt_lin) : qt_lin;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
-  const int q0 = qt * BR;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;                 // first row of this wave
+  const int qrow = qw0 + col;                     // this lane's query row
   const size_t qoff = (size_t)bh * a.Tq;
   const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
-  const uint16_t* __restrict__ Kp = a.k + kvoff;
-  const uint16_t* __restrict__ Vp = a.v + kvoff;
-
   const int shift = a.Tk - a.Tq;
   int kv_end = a.Tk;
-  if (CAUSAL) kv_end = min(a.Tk, q0 + BR + shift);
+  if (CAUSAL) kv_end = min(a.Tk, q0 + C::BR + shift);
   const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
-  const int qrow = q0 + wave * 32 + col;
-  const bool live = qrow < a.Tq;
+  // Q and dO rows of this lane's query (B operands), its lse2 and D.
   bf16x8 qf[D / 16], gf[D / 16];
-  float lse2 = INFINITY, delta = 0.f;
+  float lse2, delta;
   {
-    const uint16_t* qs = a.q + (qoff + (live ? qrow : 0)) * D + 8 * half;
-    const uint16_t* gs = a.dout + (qoff + (live ? qrow : 0)) * D + 8 * half;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + qoff * D, (uint32_t)a.Tq * D * 2);
+    const bool live = qrow < a.Tq;
+    const uint32_t base = live ? (uint32_t)(qrow * D + 8 * half) * 2 : kOutOfRange;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      qf[s] = as_bf16x8(live ? global_load_b128(qs + s * 16) : u32x4{0, 0, 0, 0});
-      gf[s] = as_bf16x8(live ? global_load_b128(gs + s * 16) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = as_bf16x8(buf_load_b128(qrs, base + ks * 32));
+      gf[ks] = as_bf16x8(buf_load_b128(grs, base + ks * 32));
     }
-    if (live) {
-      const float2 st = *(const float2*)(a.stats + 2 * (qoff + qrow));
-      lse2 = st.x;
-      delta = st.y;
-    }
+    // rows past Tq: Q = dO = 0, so dS = 0 whatever these two hold
+    const float2 st = live ? *(const float2*)(a.stats + 2 * (qoff + qrow)) : float2{0.f, 0.f};
+    lse2 = st.x;
+    delta = st.y;
   }
 
   f32x16 dq_acc[D / 32];
@@ -345,107 +372,107 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
 
-  u32x4 kst[LOADS], vst[LOADS];
-  auto load_tile = [&](int j) {
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_row[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  bool dma_is_v[C::DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / CH, ch = c % CH;
-      const int kr = j * BC + row;
-      if (kr < a.Tk) {
-        kst[i] = global_load_b128(Kp + (size_t)kr * D + ch * 8);
-        vst[i] = global_load_b128(Vp + (size_t)kr * D + ch * 8);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
-    FA_LDS uint8_t* vb = kb + TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / CH, ch = c % CH;
-      lds_write_b128(kb, row * PITCH + ch * 16, kst[i]);
-      lds_write_b128(vb, row * PITCH + ch * 16, vst[i]);
-    }
-  };
-
-  if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int n = wave * C::DMA_PER_WAVE + i;
+    const int m = n % (C::TILE_DMA / 2);
+    dma_is_v[i] = n >= C::TILE_DMA / 2;
+    const int p = 64 * m + lane;
+    const int r = p / CH, pc = p % CH;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+    dma_dst[i] = (dma_is_v[i] ? KTILE : 0) + m * 1024;
   }
-  __syncthreads();
+  auto issue = [&](int j, int stage) {
+    FA_LDS uint8_t* st = smem + stage * STAGE;
+    const int k0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const bool ok = j < n_kv && k0 + (int)dma_row[i] < a.Tk;
+      dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], ok ? (uint32_t)k0 * D * 2 + dma_off[i] : kOutOfRange);
+    }
+  };
 
+  const uint32_t fq = swz<D>(col);
+  const uint32_t k_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
   const int grp = lane >> 4, gi = lane & 15;
   const int tr_row = 4 * (grp >> 1) + (gi >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
+  const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
+  const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
+  const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
+  const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
   const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
 
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_kv) load_tile(j + 1);
-    const FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
-    const FA_LDS uint8_t* vb = kb + TILE;
-
-    f32x16 s[BC / 32], dp[BC / 32];
+  auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) {
+    const FA_LDS uint8_t* kt = st;
+    const FA_LDS uint8_t* vt = st + KTILE;
+    f32x16 s[KB], dp[KB];
 #pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[kb_i][r] = 0.f;
-        dp[kb_i][r] = 0.f;
+        s[kb][r] = 0.f;
+        dp[kb][r] = 0.f;
       }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const int off = (kb_i * 32 + col) * PITCH + (ks * 16 + 8 * half) * 2;
-        s[kb_i] = mfma32(as_bf16x8(lds_read_b128(kb, off)), qf[ks], s[kb_i]);
-        dp[kb_i] = mfma32(as_bf16x8(lds_read_b128(vb, off)), gf[ks], dp[kb_i]);
+        const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
+        s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], s[kb]);
+        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], dp[kb]);
       }
     }
-
-    const int key_base = j * BC;
-    const bool need_mask = (key_base + BC > a.Tk) ||
-                           (CAUSAL && key_base + BC - 1 > q0 + wave * 32 + shift);
-    uint32_t dsw[BC / 32][8];
+    uint32_t dsw[KB][8];
 #pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float p0 = exp2_fast(fmaf(s[kb_i][r], a.c, -lse2));
-        float p1 = exp2_fast(fmaf(s[kb_i][r + 1], a.c, -lse2));
-        if (need_mask) {
-          const int kr = key_base + kb_i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        float p0 = exp2_fast(fmaf(s[kb][r], a.c, -lse2));
+        float p1 = exp2_fast(fmaf(s[kb][r + 1], a.c, -lse2));
+        if constexpr (decltype(masked)::value) {
+          const int kr = j * BC + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           if (kr > lim) p0 = 0.f;
           if (kr + 1 > lim) p1 = 0.f;
         }
-        dsw[kb_i][r >> 1] = pack_bf16x2(p0 * (dp[kb_i][r] - delta), p1 * (dp[kb_i][r + 1] - delta));
+        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp[kb][r] - delta), p1 * (dp[kb][r + 1] - delta));
       }
-
-    // dQ^T[d, query] += K^T[d, key] dS^T[key, query]
+    // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
 #pragma unroll
-    for (int kb_i = 0; kb_i < BC / 32; ++kb_i)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 sb = as_bf16x8(u32x4{dsw[kb_i][4 * hs], dsw[kb_i][4 * hs + 1],
-                                          dsw[kb_i][4 * hs + 2], dsw[kb_i][4 * hs + 3]});
-        const int row = kb_i * 32 + hs * 16 + tr_row;
+        const bf16x8 sb = as_bf16x8(u32x4{dsw[kb][4 * hs], dsw[kb][4 * hs + 1], dsw[kb][4 * hs + 2], dsw[kb][4 * hs + 3]});
+        const uint32_t rb = (kb * 32 + hs * 16) * ROWB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int cb = (db * 32 + tr_col) * 2;
-          const u32x2 lo = lds_read_tr(kb, row * PITCH + cb);
-          const u32x2 hi = lds_read_tr(kb, (row + 8) * PITCH + cb);
+          const u32x2 lo = lds_read_tr(kt, rb + (tr_lo ^ (64 * db)));
+          const u32x2 hi = lds_read_tr(kt, rb + (tr_hi ^ (64 * db)));
           dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
         }
       }
+  };
 
-    if (j + 1 < n_kv) store_tile(buf ^ 1);
-    __syncthreads();
+  if (n_kv > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    wait_vm_barrier<C::DMA_PER_WAVE>();   // Q/dO rows, statistics and tile 0 have landed
+  }
+  int cur_stage = 0, ld_stage = 2;
+  for (int j = 0; j < n_kv; ++j) {
+    issue(j + 2, ld_stage);
+    const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
+    // some (row, key) pair of this wave is masked
+    if (CAUSAL && j * BC + BC - 1 > qw0 + shift) body(st, j, std::true_type{});
+    else body(st, j, std::false_type{});
+    wait_vm_barrier<C::DMA_PER_WAVE>();
+    cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
+    ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
   }
 
-  if (live) {
+  if (qrow < a.Tq) {
     uint16_t* dst = a.dq + (qoff + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -474,8 +501,8 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
                      a, n_ktiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_qtiles = (a.Tq + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(256), 0, stream,
+  const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
                      a, n_qtiles);
   return hipGetLastError();
 }
