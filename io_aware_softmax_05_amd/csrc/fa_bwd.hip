@@ -64,7 +64,8 @@ struct DkdvCfg {
   static constexpr int NW = D == 64 ? 8 : 4;         // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int BK = 32 * NW;                 // keys per workgroup (32 per wave)
-  static constexpr int BQ = 32;                      // query rows per tile
+  static constexpr int BQ = D == 64 ? 64 : 32;       // query rows per tile
+  static constexpr int QB = BQ / 32;                 // 32-row blocks per tile
   static constexpr int ROWB = 2 * D;                 // LDS bytes per row (swizzled, unpadded)
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int QTILE = BQ * ROWB;            // one Q (or dO) tile
@@ -73,7 +74,8 @@ struct DkdvCfg {
   static constexpr int NSTAGE = 3;
   static constexpr int TILE_DMA = 2 * BQ * CH / 64;  // 128-bit wave loads per tile (Q and dO)
   static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
-  static constexpr int VM_PER_TILE = DMA_PER_WAVE + 1;   // + the stats load
+  static constexpr int STAT_DMA = BQ * 2 / 64;       // 32-bit wave loads of the statistics
+  static constexpr int VM_PER_TILE = DMA_PER_WAVE + STAT_DMA;
   static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
 };
 
@@ -81,7 +83,7 @@ struct DkdvCfg {
 
 // One workgroup per BK keys of one KV head; each wave owns 32 keys, with its
 // K and V rows held as MFMA B operands. The workgroup walks every query tile
-// (32 rows) of every query head of the group that can see one of its keys:
+// (BQ rows) of every query head of the group that can see one of its keys:
 //   S = Q K^T, dP = dO V^T        (A operands: Q and dO rows from LDS)
 //   P = 2^(S c - lse2), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A operands: transposed LDS reads)
@@ -92,7 +94,7 @@ struct DkdvCfg {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
   using C = DkdvCfg<D>;
-  constexpr int BQ = C::BQ, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
+  constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
 
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
     dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
     dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
   }
-  const int st_row = lane >> 1;                   // stats load: (row, lse2 or D)
+  const int st_row = lane >> 1;                   // stats loads: (row, lse2 or D)
 
   // Tile iterator for the loads (two tiles ahead of the compute).
   int ld_it = 0, ld_h = 0, ld_qi = qt_begin;
@@ -173,8 +175,11 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
       const uint32_t off = ok ? (uint32_t)q0 * D * 2 + dma_off[i] : kOutOfRange;
       dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], off);
     }
-    const bool sok = live && q0 + st_row < a.Tq;
-    dma_b32(srs, st + 2 * QTILE, sok ? (uint32_t)(q0 * 2 + lane) * 4 : kOutOfRange);
+#pragma unroll
+    for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
+      const bool sok = live && q0 + 32 * i + st_row < a.Tq;
+      dma_b32(srs, st + 2 * QTILE + 256 * i, sok ? (uint32_t)((q0 + 32 * i) * 2 + lane) * 4 : kOutOfRange);
+    }
     ++ld_it;
     if (++ld_qi == n_qt) {
       ld_qi = qt_begin;
@@ -196,59 +201,67 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
     const FA_LDS uint8_t* qt = st;
     const FA_LDS uint8_t* gt = st + QTILE;
     const FA_LDS uint8_t* stt = st + 2 * QTILE;
-    // S = Q K^T and dP = dO V^T for 32 queries x 32 keys (one key per lane).
-    f32x16 s, dp;
+    // S = Q K^T and dP = dO V^T for BQ queries x 32 keys (one key per lane).
+    f32x16 s[QB], dp[QB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
-    }
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      s = mfma32(as_bf16x8(lds_read_b128(qt, q_rd ^ (32 * ks))), kf[ks], s);
-      dp = mfma32(as_bf16x8(lds_read_b128(gt, q_rd ^ (32 * ks))), vf[ks], dp);
-    }
-    // P and dS, packed to bf16 in the accumulator order (rows 8 g4 + 4 half + e).
-    uint32_t pw[8], dsw[8];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int rq = 8 * g4 + 4 * half;
-      const f32x4 s01 = *(const FA_LDS f32x4*)(stt + rq * 8);
-      const f32x4 s23 = *(const FA_LDS f32x4*)(stt + rq * 8 + 16);
-      const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-      const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
-      float p[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g4 + e;
-        float pe = exp2_fast(fmaf(s[r], a.c, -l2[e]));
-        if constexpr (decltype(masked)::value) {
-          if (key > q0 + rq + e + shift) pe = 0.f;
-        }
-        p[e] = pe;
-        ds[e] = pe * (dp[r] - dl[e]);
+      for (int r = 0; r < 16; ++r) {
+        s[qb][r] = 0.f;
+        dp[qb][r] = 0.f;
       }
-      pw[2 * g4] = pack_bf16x2(p[0], p[1]);
-      pw[2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
-      dsw[2 * g4] = pack_bf16x2(ds[0], ds[1]);
-      dsw[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t off = qb * 32 * ROWB + (q_rd ^ (32 * ks));
+        s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], s[qb]);
+        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], dp[qb]);
+      }
     }
+    // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
+    uint32_t pw[QB][8], dsw[QB][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rq = qb * 32 + 8 * g4 + 4 * half;
+        const f32x4 s01 = *(const FA_LDS f32x4*)(stt + rq * 8);
+        const f32x4 s23 = *(const FA_LDS f32x4*)(stt + rq * 8 + 16);
+        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
+          if constexpr (decltype(masked)::value) {
+            if (key > q0 + rq + e + shift) pe = 0.f;
+          }
+          p[e] = pe;
+          ds[e] = pe * (dp[qb][r] - dl[e]);
+        }
+        pw[qb][2 * g4] = pack_bf16x2(p[0], p[1]);
+        pw[qb][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
+        dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
+        dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+      }
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const bf16x8 pb = as_bf16x8(u32x4{pw[4 * hs], pw[4 * hs + 1], pw[4 * hs + 2], pw[4 * hs + 3]});
-      const bf16x8 sb = as_bf16x8(u32x4{dsw[4 * hs], dsw[4 * hs + 1], dsw[4 * hs + 2], dsw[4 * hs + 3]});
-      const uint32_t hb = hs * 16 * ROWB;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const u32x2 glo = lds_read_tr(gt, hb + (tr_lo ^ (64 * db)));
-        const u32x2 ghi = lds_read_tr(gt, hb + (tr_hi ^ (64 * db)));
-        dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
-        const u32x2 qlo = lds_read_tr(qt, hb + (tr_lo ^ (64 * db)));
-        const u32x2 qhi = lds_read_tr(qt, hb + (tr_hi ^ (64 * db)));
-        dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 pb = as_bf16x8(u32x4{pw[qb][4 * hs], pw[qb][4 * hs + 1], pw[qb][4 * hs + 2], pw[qb][4 * hs + 3]});
+        const bf16x8 sb = as_bf16x8(u32x4{dsw[qb][4 * hs], dsw[qb][4 * hs + 1], dsw[qb][4 * hs + 2], dsw[qb][4 * hs + 3]});
+        const uint32_t hb = (qb * 32 + hs * 16) * ROWB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2 glo = lds_read_tr(gt, hb + (tr_lo ^ (64 * db)));
+          const u32x2 ghi = lds_read_tr(gt, hb + (tr_hi ^ (64 * db)));
+          dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
+          const u32x2 qlo = lds_read_tr(qt, hb + (tr_lo ^ (64 * db)));
+          const u32x2 qhi = lds_read_tr(qt, hb + (tr_hi ^ (64 * db)));
+          dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+        }
       }
-    }
   };
 
   if (n_iter > 0) {
