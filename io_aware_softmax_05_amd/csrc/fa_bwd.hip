@@ -282,6 +282,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
     if (++cur_qi == n_qt) cur_qi = qt_begin;
   }
+  if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
   if (key < a.Tk) {
     uint16_t* dkp = a.dk + kvoff + (size_t)key * D;
@@ -484,6 +485,7 @@ __global__ __launch_bounds__(DqCfg<D>::NT, 1) void bwd_dq_kernel(BwdArgs a, int 
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
   }
+  if (n_kv > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
   if (qrow < a.Tq) {
     uint16_t* dst = a.dq + (qoff + qrow) * D;

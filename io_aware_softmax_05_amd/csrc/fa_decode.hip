@@ -7,103 +7,187 @@
 // is below the ridge": decoding does about one FLOP per cached byte, so the
 // time is set by how fast the cache streams out of HBM.
 //
-// Kernel 1 (split): one wave per (split, KV-head, query-row group, batch).
-//   The query heads that share a KV head are the rows of one 16-row MFMA
-//   tile, so every cached key and value is read from HBM exactly once. The
-//   wave walks its chunk of the cache in 32-key tiles (HBM -> registers ->
-//   LDS, double buffered) and runs the online-softmax recurrence, then
-//   stores its partial state (m, l, u).
+// Kernel 1 (split). Work items are (batch, KV head, query-row group, chunk)
+// for the chunks that hold cached keys; the item list is dense (chunks past a
+// sequence's length are not items) and is dealt round-robin to a grid of a
+// few single-wave workgroups per compute unit. Each wave streams the tiles of
+// its items back to back through a three-stage ring of direct-to-LDS loads,
+// so two 32-key K/V tiles are always in flight, also across item
+// boundaries. The query heads that share a KV head are the rows of one
+// 16-row MFMA tile, so every cached key and value is read from HBM once. Per
+// item the wave runs the online-softmax recurrence and stores the partial
+// state (m, l, u).
 // Kernel 2 (merge): per (batch, query head), folds the partial states with
 //   the same rescale rule (m* = max m_s; l = sum 2^(m_s - m*) l_s; same for
 //   u), then writes O = u / l and the log-sum-exp.
+#include <algorithm>
+
 #include "fa_common.hpp"
 #include "fa_internal.h"
 
 namespace fa {
 
-template <int D>
+namespace {
+
+template <int D, int NSTAGE_ = 3>
+struct DecCfg {
+  static constexpr int BC = 32;                  // keys per tile
+  static constexpr int ROWB = 2 * D;             // LDS bytes per row (swizzled, unpadded)
+  static constexpr int CH = D / 8;
+  static constexpr int TILE = BC * ROWB;         // one K (or V) tile
+  static constexpr int NSTAGE = NSTAGE_;
+  static constexpr int DMA = BC * CH / 64;       // wave loads per tensor per tile
+  static constexpr int VM_PER_TILE = 2 * DMA;
+  static constexpr int MAX_QDMA = 16 * CH / 64;  // wave loads of a full 16-row query group
+  static_assert((NSTAGE - 1) * (VM_PER_TILE + MAX_QDMA) < 64, "vmcnt range");
+  // LDS per stage: K tile, V tile, then the query rows of the item (G rows,
+  // at most 16, in whole 1 KiB wave loads); the size is set at launch.
+  __host__ __device__ static constexpr int stage_bytes(int rows) { return 2 * TILE + (rows * ROWB + 1023) / 1024 * 1024; }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Position in a workgroup's stream of tiles.
+struct DecCursor {
+  int item;     // index in the dense item list
+  int b;        // batch entry of `item` (items of earlier entries: `base`)
+  int base;
+  int hk, rg, c;
+  int k0, kend; // keys [k0, kend) of the item
+  int nt, t;    // tiles of the item, current tile; nt = 0 once the stream is over
+};
+
+}  // namespace
+
+template <int D, int NSTAGE>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_rowgroups) {
-  constexpr int BC = 32;                  // keys per tile
-  constexpr int PITCH = (D + 16) * 2;
-  constexpr int TILE = BC * PITCH;
-  constexpr int CH = D / 8;
-  constexpr int LOADS = BC * CH / 64;     // chunks per lane per tensor
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * 2 * TILE];
-  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+  using C = DecCfg<D, NSTAGE>;
+  constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, TILE = C::TILE;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_dyn[];
+  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_dyn;
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y / n_rowgroups, rg = blockIdx.y % n_rowgroups;
-  const int b = blockIdx.z;
-  const int G = a.Hq / a.Hkv;
-  const int L = a.seq_lens[b];
-  if (L < 1 || L > a.Tk_max) return;      // reported as NaN by the merge
-  const int k_begin = split * a.chunk;
-  if (k_begin >= L) return;               // the merge ignores splits past L
-  const int k_end = min(L, k_begin + a.chunk);
-  const int n_kv = (k_end - k_begin + BC - 1) / BC;
-
-  const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk_max * D;
-  const uint16_t* __restrict__ Kp = a.k + kvoff;
-  const uint16_t* __restrict__ Vp = a.v + kvoff;
-
-  // B operand of S^T = K q^T: lane holds query row (lane % 16), 8 dims.
   const int qcol = lane & 15, quad = lane >> 4;
-  const int g = rg * 16 + qcol;           // head index inside the group
-  const bool live = g < G;
-  const int hq = hk * G + (live ? g : 0);
-  bf16x8 qf[D / 32];
-  {
-    const uint16_t* src = a.q + ((size_t)b * a.Hq + hq) * D + 8 * quad;
+  const int G = a.Hq / a.Hkv;
+  const int groups = a.Hkv * n_rowgroups;        // items per chunk of one batch entry
+  const int q_rows = min(G, 16);                 // query rows stored per stage
+  const int STAGE = C::stage_bytes(q_rows);
+
+  // chunks of batch entry b (0 for a length outside [1, Tk_max]: the merge writes NaN)
+  auto n_chunks = [&](int b) -> int {
+    const int L = a.seq_lens[b];
+    return (L < 1 || L > a.Tk_max) ? 0 : (L + a.chunk - 1) / a.chunk;
+  };
+  auto locate = [&](DecCursor& u) {
+    while (u.b < a.B) {
+      const int cnt = n_chunks(u.b) * groups;
+      if (u.item < u.base + cnt) break;
+      u.base += cnt;
+      ++u.b;
+    }
+    if (u.b >= a.B) {
+      u.nt = 0;
+      return;
+    }
+    const int nb = n_chunks(u.b);
+    const int r = u.item - u.base;
+    const int grp = r / nb;
+    u.c = r - grp * nb;
+    u.hk = grp / n_rowgroups;
+    u.rg = grp - u.hk * n_rowgroups;
+    u.k0 = u.c * a.chunk;
+    u.kend = min(a.seq_lens[u.b], u.k0 + a.chunk);
+    u.nt = (u.kend - u.k0 + BC - 1) / BC;
+    u.t = 0;
+  };
+  auto advance = [&](DecCursor& u) {
+    if (u.nt == 0) return;
+    if (++u.t >= u.nt) {
+      u.item += gridDim.x;
+      locate(u);
+    }
+  };
+
+  // Loads: physical chunk p of a tile holds logical chunk p ^ swz(row) of its row.
+  uint32_t dma_row[C::DMA], dma_off[C::DMA];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qf[ks] = as_bf16x8(live ? global_load_b128(src + ks * 32) : u32x4{0, 0, 0, 0});
+  for (int i = 0; i < C::DMA; ++i) {
+    const int p = 64 * i + lane;
+    const int r = p / CH, pc = p % CH;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
   }
-
-  f32x4 oacc[D / 16];
+  DecCursor ld{(int)blockIdx.x, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  locate(ld);
+  DecCursor cp = ld;
+  auto issue = [&](int stage) {
+    FA_LDS uint8_t* st = smem + stage * STAGE;
+    const bool live = ld.nt > 0;
+    const size_t kvoff = live ? (size_t)(ld.b * a.Hkv + ld.hk) * a.Tk_max * D : 0;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk_max * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk_max * D * 2);
+    const int kt0 = ld.k0 + ld.t * BC;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-
-  u32x4 kst[LOADS], vst[LOADS];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 64 + lane;
-      const int row = c / CH, ch = c % CH;
-      const int key = k_begin + j * BC + row;
-      if (key < k_end) {
-        kst[i] = global_load_b128(Kp + (size_t)key * D + ch * 8);
-        vst[i] = global_load_b128(Vp + (size_t)key * D + ch * 8);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < C::DMA; ++i) {
+      const bool ok = live && kt0 + (int)dma_row[i] < ld.kend;
+      const uint32_t off = ok ? (uint32_t)kt0 * D * 2 + dma_off[i] : kOutOfRange;
+      dma_b128(krs, st + i * 1024, off);
+      dma_b128(vrs, st + TILE + i * 1024, off);
+    }
+    if (live && ld.t == 0) {
+      // first tile of an item: its query rows come along (unswizzled); a wait
+      // that counts only tile loads stays safe, it just waits a little longer
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + ((size_t)ld.b * a.Hq + ld.hk * G) * D, (uint32_t)G * D * 2);
+      // q_rows rows of CH chunks, 64 chunks (1 KiB) per wave load; lanes past
+      // the last row read out of range and write zeros inside the slot
+      for (int i = 0; i * 64 < q_rows * CH; ++i) {
+        const int p = 64 * i + lane;
+        const int r = ld.rg * 16 + p / CH;
+        const bool ok = p < q_rows * CH && p / CH + ld.rg * 16 < G;
+        dma_b128(qrs, st + 2 * TILE + i * 1024, ok ? (uint32_t)(r * D + (p % CH) * 8) * 2 : kOutOfRange);
       }
     }
-  };
-  auto store_tile = [&](int buf) {
-    FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
-    FA_LDS uint8_t* vb = kb + TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = i * 64 + lane;
-      const int row = c / CH, ch = c % CH;
-      lds_write_b128(kb, row * PITCH + ch * 16, kst[i]);
-      lds_write_b128(vb, row * PITCH + ch * 16, vst[i]);
-    }
+    advance(ld);
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
+  // LDS read offsets. K rows (A operand of S^T = K q^T): row 16 blk + qcol,
+  // chunk 4 ks + quad. V^T (A operand of O^T = V^T P^T): transposed reads of
+  // rows tr_row (+16), chunk 2 db + ((qcol >> 1) & 1).
+  const uint32_t fk = swz<D>(qcol);
+  const uint32_t k_rd = qcol * ROWB + 64 * (fk >> 2) + 16 * (quad ^ (fk & 3));            // ^ 64 ks
   const int tr_row = 4 * quad + (qcol >> 2);
-  const int tr_col = 4 * (qcol & 3);
+  const uint32_t fv = swz<D>(tr_row);
+  const uint32_t v_rd = tr_row * ROWB + 32 * (fv >> 1) + 16 * (((qcol >> 1) & 1) ^ (fv & 1)) + 8 * (qcol & 1);  // ^ 32 db
 
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_kv) load_tile(j + 1);
-    const FA_LDS uint8_t* kb = smem + buf * 2 * TILE;
+  bf16x8 qf[D / 32];
+  f32x4 oacc[D / 16];
+  float m = -INFINITY, l = 0.f;
+  bool live_row = false;
+  int hq = 0;
+
+  for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
+  int cs = 0, ls = NSTAGE - 1;
+  while (cp.nt > 0) {
+    issue(ls);
+    wait_vm<(NSTAGE - 1) * C::VM_PER_TILE>();   // the tile in stage cs has landed
+    if (cp.t == 0) {
+      // new item: query rows of this KV head's row group, fresh state
+      const int g = cp.rg * 16 + qcol;
+      live_row = g < G;
+      hq = cp.hk * G + (live_row ? g : 0);
+      const FA_LDS uint8_t* qs = smem + cs * STAGE + 2 * TILE;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qf[ks] = as_bf16x8(live_row ? lds_read_b128(qs, qcol * ROWB + (32 * ks + 8 * quad) * 2) : u32x4{0, 0, 0, 0});
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m = -INFINITY;
+      l = 0.f;
+    }
+    const FA_LDS uint8_t* kb = smem + cs * STAGE;
     const FA_LDS uint8_t* vb = kb + TILE;
 
     // S^T[key, row] for two 16-key blocks.
@@ -113,17 +197,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
       s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const u32x4 kv = lds_read_b128(kb, (blk * 16 + qcol) * PITCH + (ks * 32 + 8 * quad) * 2);
+        const u32x4 kv = lds_read_b128(kb, blk * 16 * ROWB + (k_rd ^ (64 * ks)));
         s[blk] = mfma16(as_bf16x8(kv), qf[ks], s[blk]);
       }
     }
-    const int key_base = k_begin + j * BC;
-    if (key_base + BC > k_end) {
+    const int key_base = cp.k0 + cp.t * BC;
+    if (key_base + BC > cp.kend) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (key_base + blk * 16 + 4 * quad + r >= k_end) s[blk][r] = -INFINITY;
+          if (key_base + blk * 16 + 4 * quad + r >= cp.kend) s[blk][r] = -INFINITY;
     }
 
     float mx = -INFINITY;
@@ -162,92 +246,128 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
     // 4*quad + t of block 0, k-slots 4..7 the same keys of block 1.
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const int cb = (db * 16 + tr_col) * 2;
-      const u32x2 lo = lds_read_tr(vb, tr_row * PITCH + cb);
-      const u32x2 hi = lds_read_tr(vb, (tr_row + 16) * PITCH + cb);
+      const u32x2 lo = lds_read_tr(vb, v_rd ^ (32 * db));
+      const u32x2 hi = lds_read_tr(vb, 16 * ROWB + (v_rd ^ (32 * db)));
       oacc[db] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, oacc[db]);
     }
 
-    if (j + 1 < n_kv) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Partial sum over the four lanes of the row.
-  {
-    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-    l = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-    l = pair_sum32(l);
-  }
-  if (live) {
-    const size_t pidx = ((size_t)b * a.Hq + hq) * a.n_splits + split;
-    if (quad == 0) {
-      a.part_m[pidx] = m;
-      a.part_l[pidx] = l;
-    }
-    float* u = a.part_u + pidx * D;
+    if (cp.t == cp.nt - 1) {
+      // end of the item: its partial state
+      float lt;
+      {
+        auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+        lt = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        lt = pair_sum32(lt);
+      }
+      if (live_row) {
+        const size_t pidx = ((size_t)cp.b * a.Hq + hq) * a.n_splits + cp.c;
+        if (quad == 0) {
+          a.part_m[pidx] = m;
+          a.part_l[pidx] = lt;
+        }
+        float* u = a.part_u + pidx * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) *(f32x4*)(u + db * 16 + 4 * quad) = oacc[db];
+        for (int db = 0; db < D / 16; ++db) *(f32x4*)(u + db * 16 + 4 * quad) = oacc[db];
+      }
+    }
+    advance(cp);
+    cs = cs == NSTAGE - 1 ? 0 : cs + 1;
+    ls = ls == NSTAGE - 1 ? 0 : ls + 1;
   }
+  wait_vm<0>();   // no load of this wave is left writing LDS when it exits
 }
 
-// One wave per (batch, query head); each lane owns D/64 output columns.
+// One workgroup (4 waves) per (batch, query head). Wave w folds the splits
+// s = w, w + 4, ... (the split's m and l are uniform, so they come through
+// scalar loads); each lane owns D/64 output columns. The four partial sums,
+// all relative to the same maximum, are then added through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + wave;
-  if (bh >= a.B * a.Hq) return;
+  __shared__ float red_m[4];
+  __shared__ float red_u[4][D + 1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int bh = blockIdx.x;
   const int b = bh / a.Hq;
   const int L = a.seq_lens[b];
   uint16_t* dst = a.o + (size_t)bh * D + lane * PER;
   if (L < 1 || L > a.Tk_max) {
+    if (wave == 0) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = 0x7FC0;   // quiet NaN
-    if (a.lse != nullptr && lane == 0) a.lse[bh] = __builtin_nanf("");
+      for (int e = 0; e < PER; ++e) dst[e] = 0x7FC0;   // quiet NaN
+      if (a.lse != nullptr && lane == 0) a.lse[bh] = __builtin_nanf("");
+    }
     return;
   }
   const int n_used = (L + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)bh * a.n_splits;
-  float mstar = -INFINITY;
-  for (int s = 0; s < n_used; ++s) mstar = fmaxf(mstar, a.part_m[base + s]);
+
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < n_used; s += 256) mloc = fmaxf(mloc, a.part_m[base + s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if (lane == 0) red_m[wave] = mloc;
+  __syncthreads();
+  const float mstar = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
   float lsum = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s = 0; s < n_used; ++s) {
+#pragma unroll 4
+  for (int s = wave; s < n_used; s += 4) {
     const float w = exp2_fast(a.part_m[base + s] - mstar);
-    lsum += w * a.part_l[base + s];
+    lsum = fmaf(w, a.part_l[base + s], lsum);
     const float* u = a.part_u + (base + s) * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, u[e], acc[e]);
   }
-  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) red_u[wave][lane * PER + e] = acc[e];
+  if (lane == 0) red_u[wave][D] = lsum;
+  __syncthreads();
+  if (wave != 0) return;
+  const float l_tot = red_u[0][D] + red_u[1][D] + red_u[2][D] + red_u[3][D];
+  const float inv = 1.f / l_tot;
+  float o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = lane * PER + e;
+    o[e] = (red_u[0][c] + red_u[1][c] + red_u[2][c] + red_u[3][c]) * inv;
+  }
   if (PER == 2) {
-    *(uint32_t*)dst = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
+    *(uint32_t*)dst = pack_bf16x2(o[0], o[PER - 1]);
   } else {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const uint32_t w = pack_bf16x2(acc[e] * inv, 0.f);
-      dst[e] = (uint16_t)(w & 0xffffu);
-    }
+    for (int e = 0; e < PER; ++e) dst[e] = (uint16_t)(pack_bf16x2(o[e], 0.f) & 0xffffu);
   }
-  if (a.lse != nullptr && lane == 0) a.lse[bh] = (mstar + log2_fast(lsum)) * kLn2;
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = (mstar + log2_fast(l_tot)) * kLn2;
 }
 
-template <int D>
-static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+// Split plus merge with an NSTAGE ring and WG_PER_CU resident workgroups per
+// compute unit (the grid never exceeds the item count's upper bound).
+template <int D, int NSTAGE, int WG_PER_CU>
+hipError_t launch_decode_cfg(const DecodeArgs& a, hipStream_t stream) {
+  using C = DecCfg<D, NSTAGE>;
   const int G = a.Hq / a.Hkv;
   const int n_rowgroups = (G + 15) / 16;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.n_splits, a.Hkv * n_rowgroups, a.B), dim3(64), 0, stream,
-                     a, n_rowgroups);
-  hipError_t e = hipGetLastError();
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const int nbh = a.B * a.Hq;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((nbh + 3) / 4), dim3(256), 0, stream, a);
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long slots = (long long)a.B * a.Hkv * n_rowgroups * a.n_splits;
+  const long long grid = std::min<long long>(slots, (long long)std::max(1, n_cu) * WG_PER_CU);
+  const int q_rows = std::min(G, 16);
+  const size_t lds = (size_t)NSTAGE * C::stage_bytes(q_rows);
+  hipLaunchKernelGGL((decode_split_kernel<D, NSTAGE>), dim3((unsigned)grid), dim3(64), lds, stream, a, n_rowgroups);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream) {
-  return d == 64 ? launch<64>(a, stream) : launch<128>(a, stream);
+  return d == 64 ? launch_decode_cfg<64, 3, 4>(a, stream) : launch_decode_cfg<128, 3, 3>(a, stream);
 }
 
 }  // namespace fa
