@@ -1,17 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the exact tiled-attention library on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W]
 
 One step is one pass of the hot path over one batch: fa_fwd then fa_bwd
-(recomputation from the saved LSE) at the GPT-2-medium attention shape
-(B64 H16 T1024 d64, bf16, non-causal, scale 1/8). W untimed steps, then K
-steps timed between two device synchronisations; HIP events around every
-launch, recorded on the stream the kernels run on, give per-launch durations.
+(recomputation from the saved LSE) on the GPT-2-medium attention layer
+(B64 H16 T1024 d64, bf16, non-causal, scale 1/8), with Q, K, V, dO already
+resident in HBM. W untimed steps, then K steps timed between two device
+synchronisations; HIP events recorded around every launch, on the stream the
+kernels run on, give per-launch durations.
 
 After the timed region, in the same run (not part of `value`):
   * the causal long-context forward (B1 H32 T8192 d128) and split-KV decoding
-    (B16 Hq32 Hkv8, lengths U[4096, 32768], d128) are timed the same way;
+    (B16 Hq32 Hkv8, lengths U[4096, 32768] from seed 5, d128) are timed the
+    same way;
   * the fp64 CPU oracle is timed on a bounded sample of the step's workload.
 Prints one JSON line.
 
@@ -19,10 +21,26 @@ FLOP convention: 4*d per visible (query, key) pair for the forward (two
 contractions), 2.5x that for the backward (five contractions); a causal
 square problem has T(T+1)/2 visible pairs. Decode bytes: every cached key and
 value row read once (sum_b L_b * Hkv * 2 * d * 2 bytes) plus q and o.
+
+Measured HBM traffic. `roofline.traffic` comes from profiles/hbm_traffic.json,
+written by `--record-traffic DIR` from four rocprofv3 counter runs:
+    DIR/fetch_all   rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    DIR/write_all   rocprofv3 --pmc WRITE_SIZE -- (same)
+    DIR/fetch_copy  rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --only copy --steps 2
+    DIR/write_copy  rocprofv3 --pmc WRITE_SIZE -- (same)
+(each with --output-format csv -d DIR/<name> -o run). Each counter is scaled
+by the ratio of the known copy size to what that counter reads for the plain
+1 GiB device copy. The file records a hash of the kernel sources; when the
+sources change, the traffic is reported as null until the counters are taken
+again.
 """
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,10 +51,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
-PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (AMD spec)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak (AMD spec)
 
 COPY_BYTES = 1 << 30          # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "io_aware_softmax_05_amd", "csrc")
 
 METRIC = "attention fwd/bwd TFLOPS and % of MI355X bf16 MFMA peak; decode HBM GB/s"
 
@@ -44,7 +64,16 @@ WORKLOADS = {
     # name: (B, Hq, Hkv, T, d, causal, seed)
     "gpt2-medium-fwd-bwd": (64, 16, 16, 1024, 64, False, 2),
     "causal-8k-fwd": (1, 32, 32, 8192, 128, True, 3),
-    "causal-32k-gqa-fwd-bwd": (1, 32, 8, 32768, 128, True, 4),
+}
+DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
+
+# Launch units whose HBM traffic is recorded: unit -> kernel names (prefix of
+# the demangled name, up to the argument list).
+TRAFFIC_UNITS = {
+    "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false>"],
+    "fa_bwd B64 H16 T1024 d64": ["bwd_pre_kernel<64>", "bwd_dkdv_kernel<64, false>", "bwd_dq_kernel<64, false>"],
+    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true>"],
+    "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128", "decode_merge_kernel<128>"],
 }
 
 
@@ -52,6 +81,32 @@ def fwd_flops(B, Hq, Tq, Tk, d, causal):
     pairs = Tq * (Tq + 1) // 2 if causal else Tq * Tk
     return 4.0 * d * pairs * B * Hq
 
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if p.endswith((".hip", ".hpp", ".h", ".cpp")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(unit: str):
+    """Measured HBM bytes per launch of `unit`, or None (not recorded, or the
+    kernels changed since the counters were taken)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    u = rec.get("units", {}).get(unit)
+    return None if u is None else float(u["bytes"])
+
+
+# ------------------------------------------------------------------ GPU timing
 
 def _randn_bf16(shape, gen):
     import torch
@@ -77,23 +132,17 @@ class Timer:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
 
-def attention_step_buffers(B, Hq, Hkv, T, d, seed):
+def run_attention(name, steps, warmup, backward=True):
     import torch
+    from io_aware_softmax_05_amd import fa
+    B, Hq, Hkv, T, d, causal, seed = WORKLOADS[name]
+    scale = d ** -0.5
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     q = _randn_bf16((B, Hq, T, d), gen)
     k = _randn_bf16((B, Hkv, T, d), gen)
     v = _randn_bf16((B, Hkv, T, d), gen)
     do = _randn_bf16((B, Hq, T, d), gen)
-    return q, k, v, do
-
-
-def run_attention(name, steps, warmup, backward=True):
-    import torch
-    from io_aware_softmax_05_amd import fa
-    B, Hq, Hkv, T, d, causal, seed = WORKLOADS[name]
-    scale = d ** -0.5
-    q, k, v, do = attention_step_buffers(B, Hq, Hkv, T, d, seed)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -102,39 +151,31 @@ def run_attention(name, steps, warmup, backward=True):
     stream = torch.cuda.current_stream()
     t_fwd, t_bwd = Timer(stream), Timer(stream)
 
-    def step(timed):
-        f = lambda: fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, stream)  # noqa: E731
-        b = lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d,  # noqa: E731
-                              scale, causal, stream)
-        if timed:
-            t_fwd.record(f)
-            if backward:
-                t_bwd.record(b)
-        else:
-            f()
-            if backward:
-                b()
+    def f():
+        fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, stream)
+
+    def b():
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, scale, causal, stream)
 
     for _ in range(warmup):
-        step(False)
+        f()
+        if backward:
+            b()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(True)
+        t_fwd.record(f)
+        if backward:
+            t_bwd.record(b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ff = fwd_flops(B, Hq, T, T, d, causal)
-    res = {
-        "workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "d": d, "causal": causal,
-        "wall_s": wall, "ms_per_step": wall * 1e3 / steps,
-        "fwd_ms": t_fwd.mean_ms(), "fwd_flop": ff,
-        "fwd_tflops": ff / (t_fwd.mean_ms() * 1e-3) / 1e12,
-    }
-    res["step_flop"] = ff * (3.5 if backward else 1.0)
+    res = {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "d": d, "causal": causal,
+           "wall_s": wall, "ms_per_step": wall * 1e3 / steps,
+           "fwd_ms": t_fwd.mean_ms(), "fwd_flop": ff, "step_flop": ff * (3.5 if backward else 1.0)}
     if backward:
         res["bwd_ms"] = t_bwd.mean_ms()
         res["bwd_flop"] = 2.5 * ff
-        res["bwd_tflops"] = 2.5 * ff / (t_bwd.mean_ms() * 1e-3) / 1e12
     res["host"] = {"q": q, "k": k, "v": v, "do": do}
     return res
 
@@ -142,13 +183,12 @@ def run_attention(name, steps, warmup, backward=True):
 def run_decode(steps, warmup):
     import torch
     from io_aware_softmax_05_amd import fa, inputs
-    B, Hq, Hkv, Tk_max, d = 16, 32, 8, 32768, 128
-    rng = inputs.make_rng(5)
-    lens_np = inputs.decode_lengths(rng, B)
+    B, Hq, Hkv, Tk_max, d = (DECODE[k] for k in ("B", "Hq", "Hkv", "Tk_max", "d"))
+    lens_np = inputs.decode_lengths(inputs.make_rng(DECODE["seed"]), B)
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(5)
+    gen.manual_seed(DECODE["seed"])
     q = _randn_bf16((B, Hq, d), gen)
-    kc = _randn_bf16((B, Hkv, Tk_max, d), gen)
+    kc = _randn_bf16((B, Hkv, Tk_max, d), gen)   # 1 GiB each: far larger than the 256 MiB MALL
     vc = _randn_bf16((B, Hkv, Tk_max, d), gen)
     lens = torch.from_numpy(lens_np).cuda()
     ws_bytes = fa.fa_decode_workspace_size(B, Hq, Tk_max, d)
@@ -157,8 +197,10 @@ def run_decode(steps, warmup):
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     t = Timer(stream)
-    call = lambda: fa.fa_decode_splitkv(q, kc, vc, lens, o, lse, ws, ws_bytes, B, Hq, Hkv, Tk_max, d,  # noqa: E731
-                                        d ** -0.5, 0, stream)
+
+    def call():
+        fa.fa_decode_splitkv(q, kc, vc, lens, o, lse, ws, ws_bytes, B, Hq, Hkv, Tk_max, d, d ** -0.5, 0, stream)
+
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -167,11 +209,34 @@ def run_decode(steps, warmup):
     torch.cuda.synchronize()
     kv_bytes = float(lens_np.astype(np.int64).sum()) * Hkv * 2 * d * 2
     io_bytes = 2.0 * B * Hq * d * 2
-    ms = t.mean_ms()
-    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
-    return {"workload": "split-KV decode B16 Hq32 Hkv8 Tk<=32768 d128", "ms": ms, "bytes": kv_bytes + io_bytes,
-            "sum_lengths": int(lens_np.sum()), "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+    return {"ms": t.mean_ms(), "bytes": kv_bytes + io_bytes, "sum_lengths": int(lens_np.sum())}
 
+
+def roofline(bound, work, ms, unit_name, algorithmic_bytes=None):
+    """Roofline entry for one launch unit: `work` is FLOP (bound "mfma") or
+    bytes (bound "hbm") per launch, `ms` the mean launch duration."""
+    if bound == "mfma":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    out = {"kernel": unit_name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": recorded_traffic(unit_name), "ms": round(ms, 4)}
+    if algorithmic_bytes is not None:
+        out["algorithmic_bytes"] = algorithmic_bytes
+    return out
+
+
+def bwd_algorithmic_bytes(B, Hq, Hkv, T, d):
+    """HBM bytes the backward cannot avoid: read Q, O, dO, LSE and K, V once,
+    write dQ, dK, dV, plus the per-row statistics (written once, read by the
+    two main kernels)."""
+    q_like = B * Hq * T * d * 2
+    kv_like = B * Hkv * T * d * 2
+    rows = B * Hq * T
+    return 3 * q_like + 2 * kv_like + 4 * rows + q_like + 2 * kv_like + 3 * 8 * rows
+
+
+# ------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(res, seconds):
     """The fp64 oracle, untouched, on whole (batch, head) slices of the same
@@ -192,7 +257,6 @@ def cpu_baseline(res, seconds):
         hk = hq // g
         sl = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)  # noqa: E731
         qh, kh, vh, doh = sl(h["q"], hq), sl(h["k"], hk), sl(h["v"], hk), sl(h["do"], hq)
-        t_start = time.perf_counter()
         ref.attention_fwd(qh, kh, vh, scale, causal)
         ref.attention_bwd(qh, kh, vh, doh, scale, causal)
         done += 1
@@ -206,21 +270,79 @@ def cpu_baseline(res, seconds):
                       f"{elapsed:.1f} s wall"}
 
 
+# ----------------------------------------------------------- counter records
+
+def _counter_means(path, counter):
+    """Mean per-dispatch value of `counter` for each fa:: kernel (and the
+    runtime's copy kernel) in one rocprofv3 counter_collection.csv."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if name.startswith("void fa::"):
+                key = name[len("void fa::"):].split("(")[0]
+            elif "copyBuffer" in name:
+                key = "copy"
+            else:
+                continue
+            per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def record_traffic(d):
+    def one(name, counter):
+        paths = glob.glob(os.path.join(d, name, "*counter_collection.csv"))
+        if not paths:
+            raise SystemExit(f"missing {name}/*counter_collection.csv under {d}")
+        return _counter_means(paths[0], counter)
+    fetch, write = one("fetch_all", "FETCH_SIZE"), one("write_all", "WRITE_SIZE")
+    cf, cw = one("fetch_copy", "FETCH_SIZE")["copy"], one("write_copy", "WRITE_SIZE")["copy"]
+    f_fac, w_fac = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    units = {}
+    for unit, kernels in TRAFFIC_UNITS.items():
+        ks = {}
+        total = 0.0
+        for k in kernels:
+            hits = [n for n in fetch if n.startswith(k)]
+            if not hits:
+                raise SystemExit(f"no counter record for kernel {k}")
+            n = hits[0]
+            ks[n] = {"fetch_kib": round(fetch[n], 1), "write_kib": round(write.get(n, 0.0), 1)}
+            total += fetch[n] * 1024 * f_fac + write.get(n, 0.0) * 1024 * w_fac
+        units[unit] = {"bytes": round(total), "kernels": ks}
+    rec = {"source_sha256": source_hash(),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "units": units}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
+# ---------------------------------------------------------------------- main
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2-medium-fwd-bwd", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the side measurements")
+    ap.add_argument("--no-extras", action="store_true", help="skip the causal 8k and decode measurements")
     ap.add_argument("--only", choices=["step", "causal-8k-fwd", "decode", "copy"],
                     help="run one measurement alone (profiling runs); 'copy' runs a plain device copy "
                          "of 1 GiB, the calibration for HBM byte counters")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write profiles/hbm_traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(args.record_traffic)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only (no multi-GPU path); --gpus must be 1"}))
         return 2
 
     import torch
@@ -252,40 +374,33 @@ def main():
         args.no_extras = True
         args.no_cpu_baseline = True
 
-    backward = not args.workload.endswith("-fwd")
-    res = run_attention(args.workload, args.steps, args.warmup, backward=backward)
+    res = run_attention("gpt2-medium-fwd-bwd", args.steps, args.warmup, backward=True)
+    B, Hq, Hkv, T, d = (res[k] for k in ("B", "Hq", "Hkv", "T", "d"))
     value = res["step_flop"] / (res["ms_per_step"] * 1e-3) / 1e12
-    dom_ms = res["bwd_ms"] if backward else res["fwd_ms"]
-    dom_flop = res["bwd_flop"] if backward else res["fwd_flop"]
-    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": res["workload"], "B": res["B"], "Hq": res["Hq"], "Hkv": res["Hkv"],
-                   "seq_len": res["T"], "head_dim": res["d"], "causal": res["causal"],
-                   "step": "fa_fwd + fa_bwd" if backward else "fa_fwd",
+        "config": {"workload": "GPT-2-medium attention layer fwd+bwd", "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "seq_len": T, "head_dim": d, "causal": res["causal"], "step": "fa_fwd + fa_bwd",
                    "flop_per_step": res["step_flop"]},
-        "roofline": {"kernel": ("fa_bwd launch (bwd_pre + bwd_dkdv + bwd_dq)" if backward else "fa_fwd launch"),
-                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
-        "phases": {"fwd_ms": round(res["fwd_ms"], 4), "fwd_tflops": round(res["fwd_tflops"], 2)},
+        # the dominant launch of the step: fa_bwd (its three kernels)
+        "roofline": roofline("mfma", res["bwd_flop"], res["bwd_ms"], "fa_bwd B64 H16 T1024 d64",
+                             bwd_algorithmic_bytes(B, Hq, Hkv, T, d)),
+        "phases": {"fa_fwd": roofline("mfma", res["fwd_flop"], res["fwd_ms"], "fa_fwd B64 H16 T1024 d64")},
     }
-    if backward:
-        out["phases"].update({"bwd_ms": round(res["bwd_ms"], 4), "bwd_tflops": round(res["bwd_tflops"], 2)})
     if not args.no_extras:
         torch.cuda.empty_cache()
         tgt = run_attention("causal-8k-fwd", max(10, args.steps), 3, backward=False)
         tgt.pop("host")
+        out["targets"] = {"fa_fwd causal B1 H32 T8192 d128":
+                          roofline("mfma", tgt["fwd_flop"], tgt["fwd_ms"], "fa_fwd causal B1 H32 T8192 d128")}
+        torch.cuda.empty_cache()
         dec = run_decode(max(10, args.steps), 3)
-        out["targets"] = {
-            "causal_fwd_B1_H32_T8192_d128": {"ms": round(tgt["fwd_ms"], 4), "tflops": round(tgt["fwd_tflops"], 2),
-                                             "frac_of_bf16_peak": round(tgt["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)},
-            "decode_B16_Hq32_Hkv8_Tk32768_d128": {"us": round(dec["ms"] * 1e3, 2), "GB_per_s": round(dec["GB_per_s"], 1),
-                                                  "frac_of_hbm_peak": round(dec["frac_of_hbm_peak"], 4),
-                                                  "bytes": dec["bytes"]},
-        }
+        out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"] = roofline(
+            "hbm", dec["bytes"], dec["ms"], "fa_decode_splitkv B16 Hq32 Hkv8 d128", dec["bytes"])
+        out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"]["sum_lengths"] = dec["sum_lengths"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
     print(json.dumps(out), flush=True)
