@@ -59,19 +59,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long n_row
 
 namespace {
 
-template <int D>
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = (D == 64 ? 64 : 32), int NSTAGE_ = (D == 64 ? 2 : 3)>
 struct DkdvCfg {
-  static constexpr int NW = D == 64 ? 8 : 4;         // waves per workgroup
+  static constexpr int NW = NW_;                     // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int BK = 32 * NW;                 // keys per workgroup (32 per wave)
-  static constexpr int BQ = D == 64 ? 64 : 32;       // query rows per tile
+  static constexpr int BQ = BQ_;                     // query rows per tile
   static constexpr int QB = BQ / 32;                 // 32-row blocks per tile
   static constexpr int ROWB = 2 * D;                 // LDS bytes per row (swizzled, unpadded)
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int QTILE = BQ * ROWB;            // one Q (or dO) tile
   static constexpr int STATS = BQ * 8;               // (lse2, D) per row
   static constexpr int STAGE = 2 * QTILE + STATS;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = NSTAGE_;
   static constexpr int TILE_DMA = 2 * BQ * CH / 64;  // 128-bit wave loads per tile (Q and dO)
   static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
   static constexpr int STAT_DMA = BQ * 2 / 64;       // 32-bit wave loads of the statistics
@@ -89,11 +89,11 @@ struct DkdvCfg {
 //   dV^T += dO^T P, dK^T += Q^T dS  (A operands: transposed LDS reads)
 // S puts one key per lane, so P and dS feed the second pair of products
 // straight from the accumulator registers. Q, dO and the row statistics reach
-// LDS through direct-to-LDS loads, three stages deep (two tiles in flight
-// while one is consumed); tiles are stored unpadded with an XOR swizzle.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
-  using C = DkdvCfg<D>;
+// LDS through direct-to-LDS loads into a ring of C::NSTAGE tiles (the next
+// tile loads while one is consumed; at d = 64 two stages measured fastest);
+// tiles are stored unpadded with an XOR swizzle.
+template <int D, bool CAUSAL, class C = DkdvCfg<D>>
+__global__ __launch_bounds__(C::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
@@ -264,20 +264,21 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
       }
   };
 
+  // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
+  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::VM_PER_TILE;
   if (n_iter > 0) {
-    issue(0);
-    issue(1);
-    wait_vm_barrier<C::VM_PER_TILE>();   // K/V rows and tile 0 have landed
+    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st);
+    wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
   }
-  int cur_stage = 0, ld_stage = 2, cur_qi = qt_begin;
+  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = qt_begin;
   for (int it = 0; it < n_iter; ++it) {
-    issue(ld_stage);                      // tile it+2 (zeros past the end)
+    issue(ld_stage);                      // tile it+NSTAGE-1 (zeros past the end)
     const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
     const int q0 = cur_qi * BQ;
     // some (row, key) pair of this wave is masked
     if (CAUSAL && q0 + shift < kw0 + 31) body(st, q0, std::true_type{});
     else body(st, q0, std::false_type{});
-    wait_vm_barrier<C::VM_PER_TILE>();    // tile it+1 has landed; this stage is free
+    wait_vm_barrier<AHEAD_VM>();          // tile it+1 has landed; this stage is free
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
     if (++cur_qi == n_qt) cur_qi = qt_begin;
@@ -306,17 +307,17 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(BwdArgs a, 
 
 namespace {
 
-template <int D>
+template <int D, int NW_ = 8, int BC_ = 32, int NSTAGE_ = (D == 64 ? 2 : 3)>
 struct DqCfg {
-  static constexpr int NW = 8;                        // waves per workgroup
+  static constexpr int NW = NW_;                      // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;                  // query rows per workgroup
-  static constexpr int BC = D == 64 ? 64 : 32;        // keys per tile
+  static constexpr int BC = BC_;                      // keys per tile
   static constexpr int ROWB = 2 * D;
   static constexpr int CH = D / 8;
   static constexpr int KTILE = BC * ROWB;             // one K (or V) tile
   static constexpr int STAGE = 2 * KTILE;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = NSTAGE_;
   static constexpr int TILE_DMA = 2 * BC * CH / 64;   // 128-bit wave loads per tile (K and V)
   static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
   static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
@@ -331,11 +332,10 @@ struct DqCfg {
 //   dQ^T += K^T dS^T                   (A operand: transposed reads of K)
 // The layout mirrors the forward kernel: one query per lane, so dS^T feeds
 // the last product from the accumulator registers. K and V arrive through
-// direct-to-LDS loads, three stages deep, swizzled like the dK/dV kernel's
-// tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(DqCfg<D>::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
-  using C = DqCfg<D>;
+// direct-to-LDS loads into a ring of C::NSTAGE tiles, swizzled like the
+// dK/dV kernel's tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
+template <int D, bool CAUSAL, class C = DqCfg<D>>
+__global__ __launch_bounds__(C::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
   constexpr int KB = BC / 32;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
@@ -469,19 +469,20 @@ __global__ __launch_bounds__(DqCfg<D>::NT, 1) void bwd_dq_kernel(BwdArgs a, int 
       }
   };
 
+  // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
+  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
   if (n_kv > 0) {
-    issue(0, 0);
-    issue(1, 1);
-    wait_vm_barrier<C::DMA_PER_WAVE>();   // Q/dO rows, statistics and tile 0 have landed
+    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st, st);
+    wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and tile 0 have landed
   }
-  int cur_stage = 0, ld_stage = 2;
+  int cur_stage = 0, ld_stage = C::NSTAGE - 1;
   for (int j = 0; j < n_kv; ++j) {
-    issue(j + 2, ld_stage);
+    issue(j + C::NSTAGE - 1, ld_stage);
     const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
     // some (row, key) pair of this wave is masked
     if (CAUSAL && j * BC + BC - 1 > qw0 + shift) body(st, j, std::true_type{});
     else body(st, j, std::false_type{});
-    wait_vm_barrier<C::DMA_PER_WAVE>();
+    wait_vm_barrier<AHEAD_VM>();
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
   }
