@@ -72,6 +72,6 @@ constexpr long long kMaxHeadBytes = 1ll << 31;
 
 constexpr float kLog2eHost = 1.44269504088896340736f;
 constexpr int kDecodeMinChunk = 64;
-constexpr int kDecodeAutoChunk = 512;
+constexpr int kDecodeAutoChunk = 1024;
 
 }  // namespace fa
