@@ -206,15 +206,11 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kti
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[qb][r] = 0.f;
-        dp[qb][r] = 0.f;
-      }
-#pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t off = qb * 32 * ROWB + (q_rd ^ (32 * ks));
-        s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], s[qb]);
-        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], dp[qb]);
+        // the first products start from an inline zero (no register clearing)
+        s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], ks == 0 ? f32x16{} : s[qb]);
+        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? f32x16{} : dp[qb]);
       }
     }
     // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
@@ -428,15 +424,10 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtile
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = 0.f;
-        dp[kb][r] = 0.f;
-      }
-#pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
-        s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], s[kb]);
-        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], dp[kb]);
+        s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], ks == 0 ? f32x16{} : s[kb]);
+        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? f32x16{} : dp[kb]);
       }
     }
     uint32_t dsw[KB][8];

@@ -194,11 +194,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
     f32x4 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         const u32x4 kv = lds_read_b128(kb, blk * 16 * ROWB + (k_rd ^ (64 * ks)));
-        s[blk] = mfma16(as_bf16x8(kv), qf[ks], s[blk]);
+        s[blk] = mfma16(as_bf16x8(kv), qf[ks], ks == 0 ? f32x4{} : s[blk]);
       }
     }
     const int key_base = cp.k0 + cp.t * BC;

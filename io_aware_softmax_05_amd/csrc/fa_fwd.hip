@@ -155,11 +155,10 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
 #pragma unroll
     for (int kb_i = 0; kb_i < KB; ++kb_i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb_i][r] = 0.f;
-#pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const u32x4 kv = lds_read_b128(kb, kb_i * 32 * KPITCH + ks * 32);
-        s[kb_i] = mfma32(as_bf16x8(kv), qf[ks], s[kb_i]);
+        // the first product starts from an inline zero (no register clearing)
+        s[kb_i] = mfma32(as_bf16x8(kv), qf[ks], ks == 0 ? f32x16{} : s[kb_i]);
       }
     }
   };
