@@ -38,6 +38,9 @@ BWD_SHAPES = [
     (1, 2, 2, 64, 300, 128, False),
     (1, 8, 8, 17, 17, 128, True),
     (2, 2, 1, 200, 129, 64, False),
+    (1, 6, 2, 190, 190, 64, True),      # 3 query heads per KV head, ragged 64-row tiles
+    (1, 6, 2, 300, 300, 128, False),
+    (1, 2, 2, 600, 600, 64, False),     # several 256-key workgroups and a ragged one
 ]
 
 

@@ -33,7 +33,10 @@ def _case(seed, B, Hq, Hkv, Tk_max, d, lo, hi):
 
 @pytest.mark.parametrize("shape", [(3, 8, 2, 300, 128, 1, 300), (2, 4, 4, 1000, 64, 1, 1000),
                                    (4, 32, 8, 700, 128, 60, 700), (2, 32, 1, 129, 128, 1, 129),
-                                   (1, 16, 16, 64, 64, 64, 64)],
+                                   (1, 16, 16, 64, 64, 64, 64),
+                                   (2, 24, 4, 500, 128, 1, 500),     # 6 query heads per KV head
+                                   (2, 48, 2, 400, 128, 1, 400),     # 24: a full and a partial row group
+                                   (3, 12, 4, 333, 64, 1, 333)],     # 3 query heads per KV head, d = 64
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("chunk", [0, 64, 192])
 def test_decode_parity(shape, chunk):

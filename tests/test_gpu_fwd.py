@@ -81,6 +81,8 @@ BF16_SHAPES = [
     (1, 2, 2, 17, 17, 128, True),
     (3, 2, 1, 63, 1000, 64, False),
     (1, 2, 2, 255, 64, 128, False),
+    (1, 6, 2, 333, 333, 128, True),     # 3 query heads per KV head
+    (2, 3, 3, 520, 520, 64, False),
 ]
 
 
