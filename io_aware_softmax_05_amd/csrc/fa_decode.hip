@@ -112,12 +112,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
   };
 
   // Loads: physical chunk p of a tile holds logical chunk p ^ swz(row) of its row.
-  uint32_t dma_row[C::DMA], dma_off[C::DMA];
+  uint32_t dma_off[C::DMA];
 #pragma unroll
   for (int i = 0; i < C::DMA; ++i) {
     const int p = 64 * i + lane;
     const int r = p / CH, pc = p % CH;
-    dma_row[i] = r;
     dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
   }
   DecCursor ld{(int)blockIdx.x, 0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -126,16 +125,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
   auto issue = [&](int stage) {
     FA_LDS uint8_t* st = smem + stage * STAGE;
     const bool live = ld.nt > 0;
-    const size_t kvoff = live ? (size_t)(ld.b * a.Hkv + ld.hk) * a.Tk_max * D : 0;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk_max * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk_max * D * 2);
+    // the buffer ranges end at the item's last key, so rows past it (and
+    // every row once the stream is over) read as zeros with no per-lane test
     const int kt0 = ld.k0 + ld.t * BC;
+    const size_t tile0 = live ? ((size_t)(ld.b * a.Hkv + ld.hk) * a.Tk_max + kt0) * D : 0;
+    const uint32_t bytes = live ? (uint32_t)(ld.kend - kt0) * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + tile0, bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + tile0, bytes);
 #pragma unroll
     for (int i = 0; i < C::DMA; ++i) {
-      const bool ok = live && kt0 + (int)dma_row[i] < ld.kend;
-      const uint32_t off = ok ? (uint32_t)kt0 * D * 2 + dma_off[i] : kOutOfRange;
-      dma_b128(krs, st + i * 1024, off);
-      dma_b128(vrs, st + TILE + i * 1024, off);
+      dma_b128(krs, st + i * 1024, dma_off[i]);
+      dma_b128(vrs, st + TILE + i * 1024, dma_off[i]);
     }
     if (live && ld.t == 0) {
       // first tile of an item: its query rows come along (unswizzled); a wait
@@ -219,13 +219,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
       mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
       mx = pair_max32(mx);
     }
+    // the reference maximum only moves when some row grows by more than 2^8
+    // (l and u keep a common stale reference otherwise; probabilities < 256)
     const float m_new = fmaxf(m, mx * a.c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_use);
-    m = m_new;
-    l *= alpha;
+    if (__builtin_amdgcn_ballot_w64(m_new > m + 8.f)) {
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_ref);
+      l *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float m_use = (m == -INFINITY) ? 0.f : m;
 
     uint32_t pw[4];
     float lsum = 0.f;
