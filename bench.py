@@ -283,6 +283,8 @@ def _counter_means(path, counter):
             name = r["Kernel_Name"]
             if name.startswith("void fa::"):
                 key = name[len("void fa::"):].split("(")[0]
+                if ", fa::" in key:   # drop a tuning-config template argument
+                    key = key.split(", fa::")[0] + ">"
             elif "copyBuffer" in name:
                 key = "copy"
             else:
