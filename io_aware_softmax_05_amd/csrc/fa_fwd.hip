@@ -26,14 +26,18 @@
 //   * O^T = V^T P^T: the probabilities are reused straight from the S^T
 //     accumulator layout as the B operand, V^T comes from ds_read_b64_tr_b16,
 //     and every O^T register of a lane belongs to that lane's query.
-//   * Software pipeline: while the vector unit turns S_j into probabilities
-//     and feeds them to the PV products, the matrix cores already compute
-//     S_{j+1} from the next K tile.
+//   * Two-stage software pipeline per key tile j: stage A issues the MFMAs
+//     of S_{j+1} = K_{j+1} Q^T while the vector unit turns S_j into
+//     probabilities; stage B issues O += V_j P_j while the vector unit takes
+//     the row maximum of S_{j+1}. The compiler's MFMA/exp interleave strategy
+//     (iglp 2) orders the instructions of each stage.
 //   * The running maximum is only moved when some row of the wave grows by
 //     more than 2^8; otherwise the stale maximum is kept, the probabilities
 //     stay below 256 and l and u need no rescale (the result is the same up
 //     to rounding, since l and u always share one reference).
-//   * exponentials are exp2 with scale*log2(e) folded into one FMA.
+//   * exponentials are exp2 with scale*log2(e) folded into one FMA; the row
+//     sum adds the fp32 probabilities, so the saved log-sum-exp keeps fp32
+//     accuracy for the backward.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -162,6 +166,27 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
       }
     }
   };
+  // keys past the causal limit or past Tk get -inf
+  auto mask = [&](int j, f32x16* s) {
+    const int key_base = j * BC;
+    const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
+#pragma unroll
+    for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key_base + kb_i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key > lim) s[kb_i][r] = -INFINITY;
+      }
+  };
+  // row maximum: in-lane over 16 keys per block, then the partner half (lane ^ 32)
+  auto rowmax = [&](const f32x16* s) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb_i][r]);
+    return pair_max32(mx);
+  };
 
   // Transposed-read coordinates of this lane inside its 16-lane group.
   const int grp = lane >> 4, gi = lane & 15;
@@ -181,47 +206,21 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
     store_k(1);
     __syncthreads();
     scores(0, s_a);
-    __syncthreads();   // every wave has read K_0 before K_2 replaces it
+    if (n_full == 0) mask(0, s_a);
+    m = rowmax(s_a) * a.c;   // l and u are still zero: nothing to rescale
+    __syncthreads();         // every wave has read K_0 before K_2 replaces it
   }
 
-  // One tile: softmax of s_cur (S_j) and u += P V_j, with S_{j+1} -> s_nxt.
-  auto body = [&](int j, auto masked, auto has_next, f32x16* s_cur, f32x16* s_nxt) {
+  // Tile j (s_cur = S_j, masked; m covers it): P_j and O += V_j P_j, while
+  // S_{j+1} goes to s_nxt, is masked if needed, and its row max moves m.
+  auto body = [&](int j, auto next_masked, auto has_next, f32x16* s_cur, f32x16* s_nxt) {
+    constexpr bool HN = decltype(has_next)::value;
     load_k(j + 2);
     load_v(j + 1);
-    if constexpr (decltype(masked)::value) {
-      const int key_base = j * BC;
-      const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
-#pragma unroll
-      for (int kb_i = 0; kb_i < KB; ++kb_i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key_base + kb_i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > lim) s_cur[kb_i][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb_i = 0; kb_i < KB; ++kb_i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb_i][r]);
-    mx = pair_max32(mx);
-    const float m_new = fmaxf(m, mx * a.c);
-    if (__builtin_amdgcn_ballot_w64(m_new > m + kRescaleSlack)) {
-      // move the reference: l and u are rescaled together
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_ref);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m = m_new;
-    }
     const float m_ref = (m == -INFINITY) ? 0.f : m;
-    if constexpr (decltype(has_next)::value) scores((j + 1) & 1, s_nxt);
-
-    // P = 2^(S*c - m), 16 keys at a time, each block feeding its PV products.
-    const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
+    // stage A: S_{j+1} on the matrix cores, P_j = 2^(S_j c - m) on the vector unit
+    if constexpr (HN) scores((j + 1) & 1, s_nxt);
+    bf16x8 pb[KB * 2];
     float lsum = 0.f;
 #pragma unroll
     for (int kb_i = 0; kb_i < KB; ++kb_i)
@@ -236,35 +235,62 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
           lsum += p0 + p1;
           pw[e] = pack_bf16x2(p0, p1);
         }
-        const bf16x8 pb = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+        pb[kb_i * 2 + hs] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+      }
+    __builtin_amdgcn_iglp_opt(2);
+    // stage B: O^T[d, query] += V^T[d, key] P^T[key, query], 16 keys per step
+    const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
+#pragma unroll
+    for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
         const int row = kb_i * 32 + hs * 16;
-        // O^T[d, query] += V^T[d, key] P^T[key, query] for these 16 keys
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const u32x2 lo = lds_read_tr(vb, row * VPITCH + db * 64);
           const u32x2 hi = lds_read_tr(vb, (row + 8) * VPITCH + db * 64);
-          oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, oacc[db]);
+          oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kb_i * 2 + hs], oacc[db]);
         }
       }
     l += lsum;
-    if constexpr (decltype(has_next)::value) {
+    if constexpr (HN) {
+      if constexpr (decltype(next_masked)::value) mask(j + 1, s_nxt);
+      const float m_new = fmaxf(m, rowmax(s_nxt) * a.c);
+      const bool move = __builtin_amdgcn_ballot_w64(m_new > m + kRescaleSlack) != 0;
       store_k(j & 1);
       store_v((j + 1) & 1);
+      if (move) {
+        // move the reference: l and u are rescaled together (after O += V_j P_j)
+        const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m = m_new;
+      }
       __syncthreads();
     }
   };
 
+  // Unrolled by two so that the score registers swap roles without copies;
+  // after the tiles every row sees completely, each next tile is masked (a
+  // complete tile passes through the mask unchanged).
   int j = 0;
-  for (; j + 2 <= n_full; j += 2) {   // unrolled by two: the score registers swap roles
+  for (; j + 2 < n_full; j += 2) {
     body(j, std::false_type{}, std::true_type{}, s_a, s_b);
     body(j + 1, std::false_type{}, std::true_type{}, s_b, s_a);
   }
-  for (; j < n_kv - 1; ++j) {
+  for (; j + 2 < n_kv; j += 2) {
     body(j, std::true_type{}, std::true_type{}, s_a, s_b);
-#pragma unroll
-    for (int kb_i = 0; kb_i < KB; ++kb_i) s_a[kb_i] = s_b[kb_i];
+    body(j + 1, std::true_type{}, std::true_type{}, s_b, s_a);
   }
-  if (n_kv > 0) body(n_kv - 1, std::true_type{}, std::false_type{}, s_a, s_b);
+  if (j + 1 < n_kv) {
+    body(j, std::true_type{}, std::true_type{}, s_a, s_b);
+    body(j + 1, std::true_type{}, std::false_type{}, s_b, s_a);
+  } else if (j < n_kv) {
+    body(j, std::true_type{}, std::false_type{}, s_a, s_b);
+  }
 
   const float l_tot = pair_sum32(l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
