@@ -71,7 +71,7 @@ DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
 # the demangled name, up to the argument list).
 TRAFFIC_UNITS = {
     "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false>"],
-    "fa_bwd B64 H16 T1024 d64": ["bwd_pre_kernel<64>", "bwd_dkdv_kernel<64, false>", "bwd_dq_kernel<64, false>"],
+    "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false>", "bwd_dkdv_kernel<64, false>"],
     "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true>"],
     "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128", "decode_merge_kernel<128>"],
 }
@@ -228,12 +228,12 @@ def roofline(bound, work, ms, unit_name, algorithmic_bytes=None):
 
 def bwd_algorithmic_bytes(B, Hq, Hkv, T, d):
     """HBM bytes the backward cannot avoid: read Q, O, dO, LSE and K, V once,
-    write dQ, dK, dV, plus the per-row statistics (written once, read by the
-    two main kernels)."""
+    write dQ, dK, dV, plus the per-row statistics (written once by the dQ
+    kernel, read once by the dK/dV kernel)."""
     q_like = B * Hq * T * d * 2
     kv_like = B * Hkv * T * d * 2
     rows = B * Hq * T
-    return 3 * q_like + 2 * kv_like + 4 * rows + q_like + 2 * kv_like + 3 * 8 * rows
+    return 3 * q_like + 2 * kv_like + 4 * rows + q_like + 2 * kv_like + 2 * 8 * rows
 
 
 # ------------------------------------------------------------- CPU baseline

@@ -9,51 +9,22 @@
 // from dS, with the softmax Jacobian dS_ij = P_ij (dP_ij - D_i) and
 // D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic.
 //
-// Three kernels, no atomics (the result is deterministic):
-//   pre   D_i = rowsum(dO * O) in fp32 (HBM bound, one pass over O and dO).
+// Two kernels, no atomics (the result is deterministic), dq first:
+//   dq    one workgroup per 128 query rows, laid out like the forward
+//         (S^T = K Q^T, one query per lane): dQ^T = K^T dS^T with K^T from
+//         transposed LDS reads. Its prologue also forms each row's
+//         D_i = rowsum(dO * O) and LSE * log2(e) and stores the pair for dkdv.
 //   dkdv  one workgroup per 128 keys of a KV head (32 keys per wave, K and V
 //         fragments held in registers); it walks every query tile of every
 //         query head of the group. S = Q K^T puts one key per lane, so P and
 //         dS feed dV^T = dO^T P and dK^T = Q^T dS straight from the
 //         accumulators; dO^T and Q^T come from ds_read_b64_tr_b16.
-//   dq    one workgroup per 128 query rows, laid out like the forward
-//         (S^T = K Q^T, one query per lane): dQ^T = K^T dS^T with K^T from
-//         transposed LDS reads.
 #include <type_traits>
 
 #include "fa_common.hpp"
 #include "fa_internal.h"
 
 namespace fa {
-
-// ------------------------------------------------------------------ pre
-
-// Per query row: stats = (LSE * log2(e), D) with D = sum_c dO_c O_c; a row
-// that saw no key (LSE = -inf) gets +inf, so every rebuilt probability is 0.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long n_rows) {
-  constexpr int LPR = D / 8;                   // lanes per row (16 B each)
-  constexpr int RPB = 256 / LPR;               // rows per block
-  const int tid = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + tid / LPR;
-  const int part = tid % LPR;
-  float acc = 0.f;
-  if (row < n_rows) {
-    const u32x4 o = global_load_b128(a.o + row * D + part * 8);
-    const u32x4 g = global_load_b128(a.dout + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16_lo(o[e]), bf16_lo(g[e]), acc);
-      acc = fmaf(bf16_hi(o[e]), bf16_hi(g[e]), acc);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < n_rows && part == 0) {
-    const float l = a.lse[row];
-    *(float2*)(a.stats + 2 * row) = float2{l == -INFINITY ? INFINITY : l * kLog2e, acc};
-  }
-}
 
 // ----------------------------------------------------------------- dk dv
 
@@ -357,23 +328,38 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtile
   if (CAUSAL) kv_end = min(a.Tk, q0 + C::BR + shift);
   const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
-  // Q and dO rows of this lane's query (B operands), its lse2 and D.
+  // Q and dO rows of this lane's query (B operands; the lane holds half of
+  // the dims, lane ^ 32 the other half), its lse2 = LSE * log2(e) and
+  // D = sum_c dO_c O_c, which are also stored for the dK/dV kernel. A row
+  // that saw no key (LSE = -inf) gets lse2 = +inf, so every rebuilt
+  // probability is 0.
   bf16x8 qf[D / 16], gf[D / 16];
   float lse2, delta;
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff * D, (uint32_t)a.Tq * D * 2);
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + qoff * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.o + qoff * D, (uint32_t)a.Tq * D * 2);
     const bool live = qrow < a.Tq;
     const uint32_t base = live ? (uint32_t)(qrow * D + 8 * half) * 2 : kOutOfRange;
+    float dsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = as_bf16x8(buf_load_b128(qrs, base + ks * 32));
-      gf[ks] = as_bf16x8(buf_load_b128(grs, base + ks * 32));
+      const u32x4 qw = buf_load_b128(qrs, base + ks * 32);
+      const u32x4 gw = buf_load_b128(grs, base + ks * 32);
+      const u32x4 ow = buf_load_b128(ors, base + ks * 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = fmaf(bf16_lo(gw[e]), bf16_lo(ow[e]), dsum);
+        dsum = fmaf(bf16_hi(gw[e]), bf16_hi(ow[e]), dsum);
+      }
+      qf[ks] = as_bf16x8(qw);
+      gf[ks] = as_bf16x8(gw);
     }
-    // rows past Tq: Q = dO = 0, so dS = 0 whatever these two hold
-    const float2 st = live ? *(const float2*)(a.stats + 2 * (qoff + qrow)) : float2{0.f, 0.f};
-    lse2 = st.x;
-    delta = st.y;
+    delta = pair_sum32(dsum);
+    // rows past Tq: Q = dO = 0, so dS = 0 whatever lse2 holds
+    const float lse = live ? a.lse[qoff + qrow] : 0.f;
+    lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    if (live && half == 0) *(float2*)(a.stats + 2 * (qoff + qrow)) = float2{lse2, delta};
   }
 
   f32x16 dq_acc[D / 32];
@@ -497,20 +483,15 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtile
 
 template <int D, bool CAUSAL>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
-  const long long n_rows = (long long)a.B * a.Hq * a.Tq;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((n_rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                     a, n_rows);
+  // dq first: it also stores the per-row statistics the dK/dV kernel reads
+  const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
+                     a, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (a.Tk + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(DkdvCfg<D>::NT), 0, stream,
                      a, n_ktiles);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
-                     a, n_qtiles);
   return hipGetLastError();
 }
 
