@@ -101,6 +101,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  // grids of 32-row (32-key) granularity must fit the launch limits
+  if ((int64_t)((Tq + 31) / 32) * B * Hq > INT32_MAX || (int64_t)((Tk + 31) / 32) * B * Hkv > INT32_MAX)
+    return FA_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace) || ws_bytes < fa_bwd_workspace_size(B, Hq, Tq, d))
     return FA_ERR_WORKSPACE;
   fa::BwdArgs a{};

@@ -30,9 +30,16 @@ namespace fa {
 
 namespace {
 
-template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = (D == 64 ? 64 : 32), int NSTAGE_ = (D == 64 ? 2 : 3)>
+// d = 64: 8 waves of 32 keys, 64-row query tiles, two LDS stages; d = 128:
+// 4 waves (the dK/dV accumulators need up to 512 registers per wave), 32-row
+// tiles, three stages. The small-GEMM interleave hint (iglp 0) orders the
+// LDS reads among the MFMAs of the body.
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = (D == 64 ? 64 : 32), int NSTAGE_ = (D == 64 ? 2 : 3),
+          int IGLP_ = 0, int OCC_ = 1>
 struct DkdvCfg {
   static constexpr int NW = NW_;                     // waves per workgroup
+  static constexpr int OCC = OCC_;                   // workgroups per CU the register budget allows
+  static constexpr int IGLP = IGLP_;                 // compiler interleave strategy for the body (-1: none)
   static constexpr int NT = 64 * NW;
   static constexpr int BK = 32 * NW;                 // keys per workgroup (32 per wave)
   static constexpr int BQ = BQ_;                     // query rows per tile
@@ -64,7 +71,7 @@ struct DkdvCfg {
 // tile loads while one is consumed; at d = 64 two stages measured fastest);
 // tiles are stored unpadded with an XOR swizzle.
 template <int D, bool CAUSAL, class C = DkdvCfg<D>>
-__global__ __launch_bounds__(C::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
   constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
@@ -211,6 +218,7 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kti
         dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
         dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
       }
+    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -274,9 +282,15 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kti
 
 namespace {
 
-template <int D, int NW_ = 8, int BC_ = 32, int NSTAGE_ = (D == 64 ? 2 : 3)>
+// d = 64: 8 waves (two per SIMD at about 128 registers, so two workgroups per
+// CU); d = 128: 4 waves with up to 512 registers each (8 waves spill) and the
+// MFMA/exp interleave hint. Both measured fastest on MI355X.
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = 32, int NSTAGE_ = (D == 64 ? 2 : 3), int IGLP_ = (D == 64 ? -1 : 2),
+          int OCC_ = 1>
 struct DqCfg {
   static constexpr int NW = NW_;                      // waves per workgroup
+  static constexpr int OCC = OCC_;                    // workgroups per CU the register budget allows
+  static constexpr int IGLP = IGLP_;                  // compiler interleave strategy for the body (-1: none)
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;                  // query rows per workgroup
   static constexpr int BC = BC_;                      // keys per tile
@@ -302,7 +316,7 @@ struct DqCfg {
 // direct-to-LDS loads into a ring of C::NSTAGE tiles, swizzled like the
 // dK/dV kernel's tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
 template <int D, bool CAUSAL, class C = DqCfg<D>>
-__global__ __launch_bounds__(C::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
   constexpr int KB = BC / 32;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
@@ -430,6 +444,7 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dq_kernel(BwdArgs a, int n_qtile
         }
         dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp[kb][r] - delta), p1 * (dp[kb][r + 1] - delta));
       }
+    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
     // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
