@@ -64,6 +64,7 @@ WORKLOADS = {
     # name: (B, Hq, Hkv, T, d, causal, seed)
     "gpt2-medium-fwd-bwd": (64, 16, 16, 1024, 64, False, 2),
     "causal-8k-fwd": (1, 32, 32, 8192, 128, True, 3),
+    "causal-32k-gqa-fwd-bwd": (1, 32, 8, 32768, 128, True, 4),
 }
 DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
 
@@ -387,22 +388,29 @@ def main():
         "config": {"workload": "GPT-2-medium attention layer fwd+bwd", "B": B, "Hq": Hq, "Hkv": Hkv,
                    "seq_len": T, "head_dim": d, "causal": res["causal"], "step": "fa_fwd + fa_bwd",
                    "flop_per_step": res["step_flop"]},
-        # the dominant launch of the step: fa_bwd (its three kernels)
+        # the dominant launch of the step: fa_bwd (its two kernels)
         "roofline": roofline("mfma", res["bwd_flop"], res["bwd_ms"], "fa_bwd B64 H16 T1024 d64",
                              bwd_algorithmic_bytes(B, Hq, Hkv, T, d)),
         "phases": {"fa_fwd": roofline("mfma", res["fwd_flop"], res["fwd_ms"], "fa_fwd B64 H16 T1024 d64")},
     }
     if not args.no_extras:
         torch.cuda.empty_cache()
-        tgt = run_attention("causal-8k-fwd", max(10, args.steps), 3, backward=False)
+        tgt = run_attention("causal-8k-fwd", max(10, args.steps), 10, backward=False)
         tgt.pop("host")
         out["targets"] = {"fa_fwd causal B1 H32 T8192 d128":
                           roofline("mfma", tgt["fwd_flop"], tgt["fwd_ms"], "fa_fwd causal B1 H32 T8192 d128")}
         torch.cuda.empty_cache()
-        dec = run_decode(max(10, args.steps), 3)
+        dec = run_decode(max(10, args.steps), 10)
         out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"] = roofline(
             "hbm", dec["bytes"], dec["ms"], "fa_decode_splitkv B16 Hq32 Hkv8 d128", dec["bytes"])
         out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"]["sum_lengths"] = dec["sum_lengths"]
+        torch.cuda.empty_cache()
+        g32 = run_attention("causal-32k-gqa-fwd-bwd", 3, 1, backward=True)
+        g32.pop("host")
+        out["targets"]["fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128"] = roofline(
+            "mfma", g32["fwd_flop"], g32["fwd_ms"], "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128")
+        out["targets"]["fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128"] = roofline(
+            "mfma", g32["bwd_flop"], g32["bwd_ms"], "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
     print(json.dumps(out), flush=True)
