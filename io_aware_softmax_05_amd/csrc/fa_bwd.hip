@@ -10,11 +10,12 @@
 // D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic.
 //
 // Two kernels, no atomics (the result is deterministic), dq first:
-//   dq    one workgroup per 128 query rows, laid out like the forward
+//   dq    one workgroup per 32 query rows per wave (8 waves at d = 64, 4 at
+//         d = 128), laid out like the forward
 //         (S^T = K Q^T, one query per lane): dQ^T = K^T dS^T with K^T from
 //         transposed LDS reads. Its prologue also forms each row's
 //         D_i = rowsum(dO * O) and LSE * log2(e) and stores the pair for dkdv.
-//   dkdv  one workgroup per 128 keys of a KV head (32 keys per wave, K and V
+//   dkdv  one workgroup per 32 keys per wave of a KV head (K and V
 //         fragments held in registers); it walks every query tile of every
 //         query head of the group. S = Q K^T puts one key per lane, so P and
 //         dS feed dV^T = dO^T P and dK^T = Q^T dS straight from the
@@ -30,12 +31,12 @@ namespace fa {
 
 namespace {
 
-// d = 64: 8 waves of 32 keys, 64-row query tiles, two LDS stages; d = 128:
-// 4 waves (the dK/dV accumulators need up to 512 registers per wave), 32-row
-// tiles, three stages. The small-GEMM interleave hint (iglp 0) orders the
-// LDS reads among the MFMAs of the body.
-template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = (D == 64 ? 64 : 32), int NSTAGE_ = (D == 64 ? 2 : 3),
-          int IGLP_ = 0, int OCC_ = 1>
+// 64-row query tiles in two LDS stages; d = 64: 8 waves of 32 keys with the
+// small-GEMM interleave hint (iglp 0) ordering the LDS reads among the MFMAs;
+// d = 128: 4 waves (the dK/dV accumulators need up to 512 registers per
+// wave; 8 waves spill) and no hint. Both measured fastest on MI355X.
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = 64, int NSTAGE_ = 2, int IGLP_ = (D == 64 ? 0 : -1),
+          int OCC_ = 1>
 struct DkdvCfg {
   static constexpr int NW = NW_;                     // waves per workgroup
   static constexpr int OCC = OCC_;                   // workgroups per CU the register budget allows
@@ -283,10 +284,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 namespace {
 
 // d = 64: 8 waves (two per SIMD at about 128 registers, so two workgroups per
-// CU); d = 128: 4 waves with up to 512 registers each (8 waves spill) and the
-// MFMA/exp interleave hint. Both measured fastest on MI355X.
-template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = 32, int NSTAGE_ = (D == 64 ? 2 : 3), int IGLP_ = (D == 64 ? -1 : 2),
-          int OCC_ = 1>
+// CU) and 32-key tiles; d = 128: 4 waves with up to 512 registers each (8
+// waves spill), 64-key tiles and the MFMA/exp interleave hint. Both measured
+// fastest on MI355X.
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = (D == 64 ? 32 : 64), int NSTAGE_ = (D == 64 ? 2 : 3),
+          int IGLP_ = (D == 64 ? -1 : 2), int OCC_ = 1>
 struct DqCfg {
   static constexpr int NW = NW_;                      // waves per workgroup
   static constexpr int OCC = OCC_;                    // workgroups per CU the register budget allows
