@@ -73,8 +73,11 @@ DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
 TRAFFIC_UNITS = {
     "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false>"],
     "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false>", "bwd_dkdv_kernel<64, false>"],
-    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true>"],
+    # the causal 8k and 32k forwards run the same kernel: told apart by grid size (threads)
+    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true>@524288"],
     "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128", "decode_merge_kernel<128>"],
+    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true>@2097152"],
+    "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true>", "bwd_dkdv_kernel<128, true>"],
 }
 
 
@@ -290,7 +293,7 @@ def _counter_means(path, counter):
                 key = "copy"
             else:
                 continue
-            per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+            per[(key, int(r["Grid_Size"]))][r["Dispatch_Id"]] += float(r["Counter_Value"])
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
@@ -301,19 +304,25 @@ def record_traffic(d):
             raise SystemExit(f"missing {name}/*counter_collection.csv under {d}")
         return _counter_means(paths[0], counter)
     fetch, write = one("fetch_all", "FETCH_SIZE"), one("write_all", "WRITE_SIZE")
-    cf, cw = one("fetch_copy", "FETCH_SIZE")["copy"], one("write_copy", "WRITE_SIZE")["copy"]
+    def copy_value(m):
+        vals = [v for (n, _), v in m.items() if n == "copy"]
+        if len(vals) != 1:
+            raise SystemExit(f"expected one copy kernel record, found {len(vals)}")
+        return vals[0]
+    cf, cw = copy_value(one("fetch_copy", "FETCH_SIZE")), copy_value(one("write_copy", "WRITE_SIZE"))
     f_fac, w_fac = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
     units = {}
     for unit, kernels in TRAFFIC_UNITS.items():
         ks = {}
         total = 0.0
-        for k in kernels:
-            hits = [n for n in fetch if n.startswith(k)]
-            if not hits:
-                raise SystemExit(f"no counter record for kernel {k}")
-            n = hits[0]
-            ks[n] = {"fetch_kib": round(fetch[n], 1), "write_kib": round(write.get(n, 0.0), 1)}
-            total += fetch[n] * 1024 * f_fac + write.get(n, 0.0) * 1024 * w_fac
+        for spec in kernels:
+            k, _, grid = spec.partition("@")
+            hits = [nk for nk in fetch if nk[0].startswith(k) and (not grid or nk[1] == int(grid))]
+            if len(hits) != 1:
+                raise SystemExit(f"{len(hits)} counter records match kernel {spec}: {hits}")
+            nk = hits[0]
+            ks[f"{nk[0]} grid {nk[1]}"] = {"fetch_kib": round(fetch[nk], 1), "write_kib": round(write.get(nk, 0.0), 1)}
+            total += fetch[nk] * 1024 * f_fac + write.get(nk, 0.0) * 1024 * w_fac
         units[unit] = {"bytes": round(total), "kernels": ks}
     rec = {"source_sha256": source_hash(),
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
