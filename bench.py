@@ -135,6 +135,9 @@ class Timer:
     def mean_ms(self):
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
+    def median_ms(self):
+        return float(np.median([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+
 
 def run_attention(name, steps, warmup, backward=True):
     import torch
@@ -176,9 +179,11 @@ def run_attention(name, steps, warmup, backward=True):
     ff = fwd_flops(B, Hq, T, T, d, causal)
     res = {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "d": d, "causal": causal,
            "wall_s": wall, "ms_per_step": wall * 1e3 / steps,
-           "fwd_ms": t_fwd.mean_ms(), "fwd_flop": ff, "step_flop": ff * (3.5 if backward else 1.0)}
+           "fwd_ms": t_fwd.mean_ms(), "fwd_median_ms": t_fwd.median_ms(), "fwd_flop": ff,
+           "step_flop": ff * (3.5 if backward else 1.0)}
     if backward:
         res["bwd_ms"] = t_bwd.mean_ms()
+        res["bwd_median_ms"] = t_bwd.median_ms()
         res["bwd_flop"] = 2.5 * ff
     res["host"] = {"q": q, "k": k, "v": v, "do": do}
     return res
@@ -213,7 +218,32 @@ def run_decode(steps, warmup):
     torch.cuda.synchronize()
     kv_bytes = float(lens_np.astype(np.int64).sum()) * Hkv * 2 * d * 2
     io_bytes = 2.0 * B * Hq * d * 2
-    return {"ms": t.mean_ms(), "bytes": kv_bytes + io_bytes, "sum_lengths": int(lens_np.sum())}
+    return {"ms": t.mean_ms(), "median_ms": t.median_ms(), "bytes": kv_bytes + io_bytes,
+            "sum_lengths": int(lens_np.sum())}
+
+
+def run_small_f32(steps, warmup):
+    """The single-head fp32 workload (B1 H1 T256 d64): latency only."""
+    import torch
+    from io_aware_softmax_05_amd import fa
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    q, k, v = (torch.randn((1, 1, 256, 64), generator=gen, device="cuda", dtype=torch.float32) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, 256), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    t = Timer(stream)
+
+    def call():
+        fa.fa_fwd_f32(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 0.125, False, stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        t.record(call)
+    torch.cuda.synchronize()
+    return {"median_ms": t.median_ms(), "flop": fwd_flops(1, 1, 256, 256, 64, False)}
 
 
 def roofline(bound, work, ms, unit_name, algorithmic_bytes=None):
@@ -404,14 +434,15 @@ def main():
     }
     if not args.no_extras:
         torch.cuda.empty_cache()
-        tgt = run_attention("causal-8k-fwd", max(10, args.steps), 10, backward=False)
+        # the targets: 10 untimed launches, then the median of 50 timed ones
+        tgt = run_attention("causal-8k-fwd", 50, 10, backward=False)
         tgt.pop("host")
         out["targets"] = {"fa_fwd causal B1 H32 T8192 d128":
-                          roofline("mfma", tgt["fwd_flop"], tgt["fwd_ms"], "fa_fwd causal B1 H32 T8192 d128")}
+                          roofline("mfma", tgt["fwd_flop"], tgt["fwd_median_ms"], "fa_fwd causal B1 H32 T8192 d128")}
         torch.cuda.empty_cache()
-        dec = run_decode(max(10, args.steps), 10)
+        dec = run_decode(50, 10)
         out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"] = roofline(
-            "hbm", dec["bytes"], dec["ms"], "fa_decode_splitkv B16 Hq32 Hkv8 d128", dec["bytes"])
+            "hbm", dec["bytes"], dec["median_ms"], "fa_decode_splitkv B16 Hq32 Hkv8 d128", dec["bytes"])
         out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"]["sum_lengths"] = dec["sum_lengths"]
         torch.cuda.empty_cache()
         g32 = run_attention("causal-32k-gqa-fwd-bwd", 3, 1, backward=True)
@@ -420,6 +451,9 @@ def main():
             "mfma", g32["fwd_flop"], g32["fwd_ms"], "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128")
         out["targets"]["fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128"] = roofline(
             "mfma", g32["bwd_flop"], g32["bwd_ms"], "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128")
+        f32 = run_small_f32(50, 10)
+        out["latency"] = {"fa_fwd_f32 B1 H1 T256 d64": {"median_us": round(f32["median_ms"] * 1e3, 2),
+                                                        "flop": f32["flop"], "bound": "latency"}}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
     print(json.dumps(out), flush=True)
