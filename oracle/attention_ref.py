@@ -29,7 +29,13 @@ Readings taken where the pages are silent (each is pinned by a test):
   * the softmax backward is the textbook Jacobian:
     dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik);
   * grouped KV heads are contiguous groups: query head h uses KV head
-    h // (Hq // Hkv); dK and dV sum over the group.
+    h // (Hq // Hkv); dK and dV sum over the group;
+  * a sliding window (aimlrounds "FlashAttention", section "In practice",
+    lists sliding windows among the masks the method works with, without a
+    definition) of W >= 1 keys is read as a causal band: key j is visible to query
+    i iff i + (Tk - Tq) - W < j <= i + (Tk - Tq), i.e. each query sees its
+    own position and the W - 1 keys before it; in decoding the one query
+    sees the last W cached keys. W = 0 means no window.
 
 Rows are independent, so every function may work on any subset of query rows
 (the full-size checks evaluate sampled rows one block at a time). Keys are
@@ -42,24 +48,29 @@ import numpy as np
 _ROW_BLOCK = 512
 
 
-def visible(rows: np.ndarray, Tq: int, Tk: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), Tk]: may query row i look at key j."""
+def visible(rows: np.ndarray, Tq: int, Tk: int, causal: bool, window: int = 0) -> np.ndarray:
+    """Boolean [len(rows), Tk]: may query row i look at key j (a window needs causal)."""
     rows = np.asarray(rows, dtype=np.int64)
     if not causal:
+        assert window == 0, "a sliding window is a causal band"
         return np.ones((rows.shape[0], Tk), dtype=bool)
     j = np.arange(Tk, dtype=np.int64)
-    return j[None, :] <= rows[:, None] + (Tk - Tq)
+    last = rows[:, None] + (Tk - Tq)
+    vis = j[None, :] <= last
+    if window > 0:
+        vis &= j[None, :] > last - window
+    return vis
 
 
 def row_probs(q_rows: np.ndarray, k: np.ndarray, scale: float, rows: np.ndarray,
-              Tq: int, causal: bool):
+              Tq: int, causal: bool, window: int = 0):
     """Scores, probabilities and log-sum-exp for some query rows of one head.
 
     q_rows [n,d], k [Tk,d] (fp64). Returns P [n,Tk] (zero where masked and for
     empty rows) and lse [n] (-inf for empty rows)."""
     Tk = k.shape[0]
     s = scale * (q_rows @ k.T)
-    vis = visible(rows, Tq, Tk, causal)
+    vis = visible(rows, Tq, Tk, causal, window)
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)
     empty = ~np.isfinite(m)
@@ -76,7 +87,7 @@ def _kv_head(hq: int, Hq: int, Hkv: int) -> int:
     return hq // (Hq // Hkv)
 
 
-def attention_fwd(q, k, v, scale: float, causal: bool, rows=None):
+def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, window: int = 0):
     """Forward: O [B,Hq,n,d] and LSE [B,Hq,n] for query rows `rows` (all if None).
 
     q [B,Hq,Tq,d]; k, v [B,Hkv,Tk,d]; any float dtype, computed in fp64."""
@@ -94,13 +105,13 @@ def attention_fwd(q, k, v, scale: float, causal: bool, rows=None):
             hk = _kv_head(h, Hq, Hkv)
             for s in range(0, rows.shape[0], _ROW_BLOCK):
                 r = rows[s:s + _ROW_BLOCK]
-                p, l = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal)
+                p, l = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal, window)
                 o[b, h, s:s + _ROW_BLOCK] = p @ v[b, hk]
                 lse[b, h, s:s + _ROW_BLOCK] = l
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale: float, causal: bool):
+def attention_bwd(q, k, v, do, scale: float, causal: bool, window: int = 0):
     """Backward of O = softmax(scale Q K^T [+mask]) V given dO.
 
     Returns dQ [B,Hq,Tq,d], dK and dV [B,Hkv,Tk,d] in fp64. P is recomputed
@@ -119,7 +130,7 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool):
             hk = _kv_head(h, Hq, Hkv)
             for s in range(0, Tq, _ROW_BLOCK):
                 r = np.arange(s, min(Tq, s + _ROW_BLOCK))
-                p, _ = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal)
+                p, _ = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal, window)
                 g = do[b, h, r]
                 dv[b, hk] += p.T @ g
                 dp = g @ v[b, hk].T
@@ -129,7 +140,7 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv
 
 
-def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows):
+def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows, window: int = 0):
     """dQ for some query rows of one (batch, query head): each row's gradient
     needs only that row's own scores, so it can be evaluated at any size."""
     q = np.asarray(q[b, h], dtype=np.float64)
@@ -139,14 +150,14 @@ def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: in
     vv = np.asarray(v[b, hk], dtype=np.float64)
     rows = np.asarray(rows, dtype=np.int64)
     Tq = q.shape[0]
-    p, _ = row_probs(q[rows], kk, scale, rows, Tq, causal)
+    p, _ = row_probs(q[rows], kk, scale, rows, Tq, causal, window)
     g = np.asarray(do[b, h], dtype=np.float64)[rows]
     dp = g @ vv.T
     ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     return scale * (ds @ kk)
 
 
-def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk: int, keys):
+def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk: int, keys, window: int = 0):
     """dK and dV for some keys of one (batch, KV head).
 
     A key's gradient sums contributions of every query row of the group that
@@ -160,17 +171,19 @@ def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk:
     vv = np.asarray(v[b, hk], dtype=np.float64)
     keys = np.asarray(keys, dtype=np.int64)
     Tk = kk.shape[0]
-    first = 0
+    first, stop = 0, Tq
     if causal:
         first = max(0, int(keys.min()) - (Tk - Tq))
+    if window > 0:   # rows past the last key's window see none of these keys
+        stop = max(first, min(Tq, int(keys.max()) - (Tk - Tq) + window))
     dk = np.zeros((keys.shape[0], kk.shape[1]))
     dv = np.zeros((keys.shape[0], vv.shape[1]))
     for h in range(hk * g, (hk + 1) * g):
         qq = np.asarray(q[b, h], dtype=np.float64)
         gg = np.asarray(do[b, h], dtype=np.float64)
-        for s in range(first, Tq, _ROW_BLOCK):
-            r = np.arange(s, min(Tq, s + _ROW_BLOCK))
-            p, _ = row_probs(qq[r], kk, scale, r, Tq, causal)
+        for s in range(first, stop, _ROW_BLOCK):
+            r = np.arange(s, min(stop, s + _ROW_BLOCK))
+            p, _ = row_probs(qq[r], kk, scale, r, Tq, causal, window)
             dp = gg[r] @ vv.T
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dv += p[:, keys].T @ gg[r]
@@ -178,8 +191,9 @@ def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk:
     return dk, dv
 
 
-def decode(q, k_cache, v_cache, seq_lens, scale: float, heads=None):
-    """One query token per (batch, head) against the first seq_lens[b] cached keys.
+def decode(q, k_cache, v_cache, seq_lens, scale: float, heads=None, window: int = 0):
+    """One query token per (batch, head) against the first seq_lens[b] cached keys
+    (only the last `window` of them when window > 0).
 
     q [B,Hq,d]; caches [B,Hkv,Tk_max,d]. Returns O [B,Hq,d] and LSE [B,Hq];
     `heads` optionally limits the work to a list of (b, hq) pairs (others 0)."""
@@ -190,9 +204,10 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, heads=None):
     pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
     for b, h in pairs:
         L = int(seq_lens[b])
+        lo = max(0, L - window) if window > 0 else 0
         hk = _kv_head(h, Hq, Hkv)
-        kk = np.asarray(k_cache[b, hk, :L], dtype=np.float64)
-        vv = np.asarray(v_cache[b, hk, :L], dtype=np.float64)
+        kk = np.asarray(k_cache[b, hk, lo:L], dtype=np.float64)
+        vv = np.asarray(v_cache[b, hk, lo:L], dtype=np.float64)
         qq = np.asarray(q[b, h], dtype=np.float64)[None, :]
         p, l = row_probs(qq, kk, scale, np.zeros(1, dtype=np.int64), 1, False)
         o[b, h] = (p @ vv)[0]
