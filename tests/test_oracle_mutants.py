@@ -34,8 +34,8 @@ def _fails_some_forward_pin(mod) -> bool:
 FWD_MUTANTS = {
     "scale dropped": ("s = scale * (q_rows @ k.T)", "s = q_rows @ k.T"),
     "keys reversed": ("s = scale * (q_rows @ k.T)", "s = scale * (q_rows @ k[::-1].T)"),
-    "diagonal excluded": ("return j[None, :] <= rows[:, None] + (Tk - Tq)", "return j[None, :] < rows[:, None] + (Tk - Tq)"),
-    "top-left causal alignment": ("return j[None, :] <= rows[:, None] + (Tk - Tq)", "return j[None, :] <= rows[:, None]"),
+    "diagonal excluded": ("vis = j[None, :] <= last", "vis = j[None, :] < last"),
+    "top-left causal alignment": ("last = rows[:, None] + (Tk - Tq)", "last = rows[:, None]"),
     "max missing from lse": ("lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))", "lse = np.where(empty, -np.inf, np.log(l_safe))"),
     "not normalised": ("p = e / l_safe[:, None]", "p = e"),
     "wrong kv head map": ("return hq // (Hq // Hkv)", "return hq % Hkv"),
@@ -94,3 +94,31 @@ def test_unmutated_backward_passes_fd():
 @pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
 def test_backward_mutant_is_caught(name):
     assert not _fd_check(_mutant(*BWD_MUTANTS[name])), name
+
+
+# A sliding-window mistake must fail the window pins (tests/test_oracle_window.py).
+WINDOW_MUTANTS = {
+    "window one key too wide": ("vis &= j[None, :] > last - window", "vis &= j[None, :] >= last - window"),
+    "window one key too narrow": ("vis &= j[None, :] > last - window", "vis &= j[None, :] > last - window + 1"),
+    "window ignored": ("vis &= j[None, :] > last - window", "pass"),
+    "decode window from the front": ("lo = max(0, L - window) if window > 0 else 0", "lo = 0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WINDOW_MUTANTS))
+def test_window_mutant_is_caught(name, monkeypatch):
+    from tests import test_oracle_window as tw
+    mod = _mutant(*WINDOW_MUTANTS[name])
+    monkeypatch.setattr(tw, "ref", mod)
+    checks = [lambda: tw.test_window_of_one_returns_the_diagonal_value(7, 7),
+              lambda: tw.test_window_of_one_returns_the_diagonal_value(4, 7),
+              lambda: tw.test_zero_queries_average_the_band(3),
+              lambda: tw.test_window_decode_is_the_forward_over_the_last_keys()]
+    failed = False
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failed = True
+            break
+    assert failed, name
