@@ -78,6 +78,20 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            hipStream_t stream);
 
 /*
+ * Causal sliding-window forward: as fa_fwd with causal set, except that query
+ * row i sees only the window of `window` keys ending at its own position,
+ * i.e. key j is visible iff i + (Tk - Tq) - window < j <= i + (Tk - Tq).
+ * The pages list sliding windows among the masks the method works with
+ * (aimlrounds "FlashAttention", section "In practice") without defining
+ * them; this band is the reading taken. Key tiles wholly outside every row's
+ * window are skipped. Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for
+ * window < 1.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int window,
+                  hipStream_t stream);
+
+/*
  * Forward pass with fp32 inputs and outputs (same parameter list and layout
  * as fa_fwd, every tensor fp32). Scores, probabilities and accumulators stay
  * in fp32 throughout: this is the accuracy reference path for small problems
@@ -120,6 +134,16 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            hipStream_t stream);
 
 /*
+ * Backward of fa_fwd_window (same band; the parameters of fa_bwd with causal
+ * replaced by window >= 1). Errors: as fa_bwd, plus FA_ERR_INVALID_ARG for
+ * window < 1.
+ */
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int window,
+                  hipStream_t stream);
+
+/*
  * Workspace bytes fa_decode_splitkv needs for KV caches of up to Tk_max
  * positions: per (batch, query head, split) one partial state (m, l, u[d])
  * in fp32, for the largest split count the library may choose. Linear in
@@ -154,6 +178,20 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t ws_bytes,
                       int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
                       hipStream_t stream);
+
+/*
+ * Split-KV decoding with a sliding window: as fa_decode_splitkv, but the
+ * query of batch entry b sees only the last `window` cached keys
+ * (positions max(0, seq_lens[b] - window) .. seq_lens[b] - 1; the band of
+ * fa_fwd_window for the query at position seq_lens[b] - 1). Chunks wholly
+ * before the window are not read. Same workspace size. Errors: as
+ * fa_decode_splitkv, plus FA_ERR_INVALID_ARG for window < 1.
+ */
+int fa_decode_splitkv_window(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seq_lens, void* o, float* lse,
+                             void* workspace, size_t ws_bytes,
+                             int B, int Hq, int Hkv, int Tk_max, int d, float scale, int window, int chunk,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

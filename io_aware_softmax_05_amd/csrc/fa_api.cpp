@@ -45,9 +45,9 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
-           hipStream_t stream) {
+static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int window,
+                    hipStream_t stream) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
   if (st != FA_OK) return st;
@@ -63,7 +63,21 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.c = scale * fa::kLog2eHost;
+  a.window = window;
   return to_status(fa::launch_fwd_bf16(a, d, causal != 0, stream));
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+           hipStream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, 0, stream);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int window,
+                  hipStream_t stream) {
+  if (window < 1) return FA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, 1, window, stream);
 }
 
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -91,10 +105,10 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d) {
   return round256((size_t)B * Hq * Tq * 2 * sizeof(float));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
-           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
-           hipStream_t stream) {
+static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                    int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int window,
+                    hipStream_t stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
   if (st != FA_OK) return st;
@@ -120,7 +134,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.scale = scale;
   a.c = scale * fa::kLog2eHost;
+  a.window = window;
   return to_status(fa::launch_bwd(a, d, causal != 0, stream));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+           hipStream_t stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale,
+                  causal, 0, stream);
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int window,
+                  hipStream_t stream) {
+  if (window < 1) return FA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale,
+                  1, window, stream);
 }
 
 size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d) {
@@ -130,11 +162,11 @@ size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d) {
   return round256(per * sizeof(float)) * 2 + round256(per * d * sizeof(float));
 }
 
-int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
-                      const int* seq_lens, void* o, float* lse,
-                      void* workspace, size_t ws_bytes,
-                      int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
-                      hipStream_t stream) {
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                       const int* seq_lens, void* o, float* lse,
+                       void* workspace, size_t ws_bytes,
+                       int B, int Hq, int Hkv, int Tk_max, int d, float scale, int window, int chunk,
+                       hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !seq_lens || !o) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, 1, Tk_max, d, scale);
   if (st != FA_OK) return st;
@@ -166,7 +198,27 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   a.chunk = chunk;
   a.n_splits = n_splits;
   a.c = scale * fa::kLog2eHost;
+  a.window = window;
   return to_status(fa::launch_decode(a, d, stream));
+}
+
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, void* o, float* lse,
+                      void* workspace, size_t ws_bytes,
+                      int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
+                      hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, o, lse, workspace, ws_bytes, B, Hq, Hkv, Tk_max, d, scale,
+                     0, chunk, stream);
+}
+
+int fa_decode_splitkv_window(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seq_lens, void* o, float* lse,
+                             void* workspace, size_t ws_bytes,
+                             int B, int Hq, int Hkv, int Tk_max, int d, float scale, int window, int chunk,
+                             hipStream_t stream) {
+  if (window < 1) return FA_ERR_INVALID_ARG;
+  return decode_impl(q, k_cache, v_cache, seq_lens, o, lse, workspace, ws_bytes, B, Hq, Hkv, Tk_max, d, scale,
+                     window, chunk, stream);
 }
 
 }  // extern "C"

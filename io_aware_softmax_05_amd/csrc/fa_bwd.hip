@@ -71,8 +71,9 @@ struct DkdvCfg {
 // LDS through direct-to-LDS loads into a ring of C::NSTAGE tiles (the next
 // tile loads while one is consumed; at d = 64 two stages measured fastest);
 // tiles are stored unpadded with an XOR swizzle.
-template <int D, bool CAUSAL, class C = DkdvCfg<D>>
+template <int D, bool CAUSAL, class C = DkdvCfg<D>, bool WIN = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+  static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
@@ -117,7 +118,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   // Query tiles that can see any key of this workgroup, for each query head of the group.
   int qt_begin = 0;
   if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
-  const int n_qt = (a.Tq + BQ - 1) / BQ;
+  int n_qt = (a.Tq + BQ - 1) / BQ;
+  if (WIN) {   // rows past the last key's window see none of these keys
+    const int last_row = k0 + C::BK - 1 - shift + a.window - 1;
+    n_qt = last_row < 0 ? 0 : min(n_qt, last_row / BQ + 1);
+  }
   const int per_head = max(0, n_qt - qt_begin);
   const int n_iter = per_head * G;
 
@@ -209,7 +214,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
           const int r = 4 * g4 + e;
           float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
           if constexpr (decltype(masked)::value) {
-            if (key > q0 + rq + e + shift) pe = 0.f;
+            const int lim = q0 + rq + e + shift;
+            if (key > lim || (WIN && key <= lim - a.window)) pe = 0.f;
           }
           p[e] = pe;
           ds[e] = pe * (dp[qb][r] - dl[e]);
@@ -251,9 +257,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     issue(ld_stage);                      // tile it+NSTAGE-1 (zeros past the end)
     const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
     const int q0 = cur_qi * BQ;
-    // some (row, key) pair of this wave is masked
-    if (CAUSAL && q0 + shift < kw0 + 31) body(st, q0, std::true_type{});
-    else body(st, q0, std::false_type{});
+    // some (row, key) pair of this wave is masked (causal limit or window start)
+    if ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0))
+      body(st, q0, std::true_type{});
+    else
+      body(st, q0, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();          // tile it+1 has landed; this stage is free
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
@@ -317,8 +325,9 @@ struct DqCfg {
 // the last product from the accumulator registers. K and V arrive through
 // direct-to-LDS loads into a ring of C::NSTAGE tiles, swizzled like the
 // dK/dV kernel's tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
-template <int D, bool CAUSAL, class C = DqCfg<D>>
+template <int D, bool CAUSAL, class C = DqCfg<D>, bool WIN = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
   constexpr int KB = BC / 32;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
@@ -418,6 +427,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
   const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
   const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
+  const int lo = WIN ? qrow + shift - a.window + 1 : 0;   // window start of this lane's row
+  // tiles before j_begin are invisible to every row of the workgroup
+  const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
 
   auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) {
     const FA_LDS uint8_t* kt = st;
@@ -441,8 +453,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
         float p1 = exp2_fast(fmaf(s[kb][r + 1], a.c, -lse2));
         if constexpr (decltype(masked)::value) {
           const int kr = j * BC + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (kr > lim) p0 = 0.f;
-          if (kr + 1 > lim) p1 = 0.f;
+          if (kr > lim || (WIN && kr < lo)) p0 = 0.f;
+          if (kr + 1 > lim || (WIN && kr + 1 < lo)) p1 = 0.f;
         }
         dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp[kb][r] - delta), p1 * (dp[kb][r + 1] - delta));
       }
@@ -465,22 +477,24 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 
   // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
   constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
-  if (n_kv > 0) {
-    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st, st);
-    wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and tile 0 have landed
+  if (j_begin < n_kv) {
+    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(j_begin + st, st);
+    wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
   }
   int cur_stage = 0, ld_stage = C::NSTAGE - 1;
-  for (int j = 0; j < n_kv; ++j) {
+  for (int j = j_begin; j < n_kv; ++j) {
     issue(j + C::NSTAGE - 1, ld_stage);
     const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
-    // some (row, key) pair of this wave is masked
-    if (CAUSAL && j * BC + BC - 1 > qw0 + shift) body(st, j, std::true_type{});
-    else body(st, j, std::false_type{});
+    // some (row, key) pair of this wave is masked (causal limit or window start)
+    if ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1))
+      body(st, j, std::true_type{});
+    else
+      body(st, j, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
   }
-  if (n_kv > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
+  if (j_begin < n_kv) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
   if (qrow < a.Tq) {
     uint16_t* dst = a.dq + (qoff + qrow) * D;
@@ -498,21 +512,22 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 
 // ---------------------------------------------------------------- launch
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN = false>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DqCfg<D>, WIN>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
                      a, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (a.Tk + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(DkdvCfg<D>::NT), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DkdvCfg<D>, WIN>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(DkdvCfg<D>::NT), 0, stream,
                      a, n_ktiles);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream) {
+  if (a.window > 0) return d == 64 ? launch<64, true, true>(a, stream) : launch<128, true, true>(a, stream);
   if (d == 64) return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
   return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }

@@ -55,8 +55,9 @@ struct DecCursor {
   int item;     // index in the dense item list
   int b;        // batch entry of `item` (items of earlier entries: `base`)
   int base;
-  int hk, rg, c;
+  int hk, rg, c;   // c: split index (chunk index minus the first chunk in use)
   int k0, kend; // keys [k0, kend) of the item
+  int klo;      // first visible key of the sequence (window start)
   int nt, t;    // tiles of the item, current tile; nt = 0 once the stream is over
 };
 
@@ -76,10 +77,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
   const int q_rows = min(G, 16);                 // query rows stored per stage
   const int STAGE = C::stage_bytes(q_rows);
 
-  // chunks of batch entry b (0 for a length outside [1, Tk_max]: the merge writes NaN)
+  // chunks of batch entry b in use (0 for a length outside [1, Tk_max]: the
+  // merge writes NaN); with a window only those meeting the last W keys
+  auto first_key = [&](int L) -> int { return a.window > 0 ? max(0, L - a.window) : 0; };
   auto n_chunks = [&](int b) -> int {
     const int L = a.seq_lens[b];
-    return (L < 1 || L > a.Tk_max) ? 0 : (L + a.chunk - 1) / a.chunk;
+    return (L < 1 || L > a.Tk_max) ? 0 : (L + a.chunk - 1) / a.chunk - first_key(L) / a.chunk;
   };
   auto locate = [&](DecCursor& u) {
     while (u.b < a.B) {
@@ -98,8 +101,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
     u.c = r - grp * nb;
     u.hk = grp / n_rowgroups;
     u.rg = grp - u.hk * n_rowgroups;
-    u.k0 = u.c * a.chunk;
-    u.kend = min(a.seq_lens[u.b], u.k0 + a.chunk);
+    const int L = a.seq_lens[u.b];
+    u.klo = first_key(L);
+    const int chunk_idx = u.klo / a.chunk + u.c;
+    u.k0 = max(chunk_idx * a.chunk, u.klo / BC * BC);   // whole tiles from the window start
+    u.kend = min(L, chunk_idx * a.chunk + a.chunk);
     u.nt = (u.kend - u.k0 + BC - 1) / BC;
     u.t = 0;
   };
@@ -201,12 +207,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
       }
     }
     const int key_base = cp.k0 + cp.t * BC;
-    if (key_base + BC > cp.kend) {
+    if (key_base + BC > cp.kend || key_base < cp.klo) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key_base + blk * 16 + 4 * quad + r >= cp.kend) s[blk][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int key = key_base + blk * 16 + 4 * quad + r;
+          if (key >= cp.kend || key < cp.klo) s[blk][r] = -INFINITY;
+        }
     }
 
     float mx = -INFINITY;
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int n_used = (L + a.chunk - 1) / a.chunk;
+  const int n_used = (L + a.chunk - 1) / a.chunk - (a.window > 0 ? max(0, L - a.window) : 0) / a.chunk;
   const size_t base = (size_t)bh * a.n_splits;
 
   float mloc = -INFINITY;

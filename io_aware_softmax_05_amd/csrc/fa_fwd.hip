@@ -67,8 +67,9 @@ constexpr float kRescaleSlack = 8.f;
 
 }  // namespace
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_kernel(FwdArgs a) {
+  static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   using C = FwdCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, NT = C::NT, CH = C::CH, LOADS = C::LOADS;
   constexpr int KPITCH = C::KPITCH, VPITCH = C::VPITCH, KTILE = C::KTILE, VTILE = C::VTILE;
@@ -102,6 +103,15 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   int n_full = a.Tk / BC;
   if (CAUSAL) n_full = min(n_full, max(0, q0 + shift + 1) / BC);
   n_full = min(n_full, n_kv - 1);
+  // Sliding window: row i sees keys (i + shift - W, i + shift]. Tiles before
+  // j_begin are invisible to every row; tiles [j_begin, j_head) hold keys
+  // below some row's window and need the mask.
+  int j_begin = 0, j_head = 0;
+  if (WIN) {
+    j_begin = min(n_kv, max(0, q0 + shift - a.window + 1) / BC);
+    const int lo_last = q0 + BR - 1 + shift - a.window + 1;   // window start of the last row
+    j_head = min(n_kv, max(j_begin, (max(0, lo_last) + BC - 1) / BC));
+  }
 
   // Q fragments: B operand of S^T = K Q^T (lane: query column, 8 dims).
   const int qrow = q0 + wave * 32 + col;
@@ -166,16 +176,17 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
       }
     }
   };
-  // keys past the causal limit or past Tk get -inf
+  // keys past the causal limit or past Tk (or before the window) get -inf
   auto mask = [&](int j, f32x16* s) {
     const int key_base = j * BC;
     const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
+    const int lo = WIN ? qrow + shift - a.window + 1 : 0;
 #pragma unroll
     for (int kb_i = 0; kb_i < KB; ++kb_i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key_base + kb_i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key > lim) s[kb_i][r] = -INFINITY;
+        if (key > lim || (WIN && key < lo)) s[kb_i][r] = -INFINITY;
       }
   };
   // row maximum: in-lane over 16 keys per block, then the partner half (lane ^ 32)
@@ -197,18 +208,19 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   // LDS ring: iteration j reads K_{j+1} from kbuf[(j+1)&1] and V_j from
   // vbuf[j&1]; it refills kbuf[j&1] with K_{j+2} and vbuf[(j+1)&1] with V_{j+1}.
   f32x16 s_a[KB], s_b[KB];
-  if (n_kv > 0) {
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-    load_k(1);
-    store_k(1);
+  const int j0 = j_begin;
+  if (j0 < n_kv) {
+    load_k(j0);
+    load_v(j0);
+    store_k(j0 & 1);
+    store_v(j0 & 1);
+    load_k(j0 + 1);
+    store_k((j0 + 1) & 1);
     __syncthreads();
-    scores(0, s_a);
-    if (n_full == 0) mask(0, s_a);
+    scores(j0 & 1, s_a);
+    if (j0 >= n_full || j0 < j_head) mask(j0, s_a);
     m = rowmax(s_a) * a.c;   // l and u are still zero: nothing to rescale
-    __syncthreads();         // every wave has read K_0 before K_2 replaces it
+    __syncthreads();         // every wave has read K_j0 before K_j0+2 replaces it
   }
 
   // Tile j (s_cur = S_j, masked; m covers it): P_j and O += V_j P_j, while
@@ -276,7 +288,14 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   // Unrolled by two so that the score registers swap roles without copies;
   // after the tiles every row sees completely, each next tile is masked (a
   // complete tile passes through the mask unchanged).
-  int j = 0;
+  int j = j0;
+  if constexpr (WIN) {   // the window's first tiles: masked, one at a time
+    for (; j + 1 < j_head; ++j) {
+      body(j, std::true_type{}, std::true_type{}, s_a, s_b);
+#pragma unroll
+      for (int kb_i = 0; kb_i < KB; ++kb_i) s_a[kb_i] = s_b[kb_i];
+    }
+  }
   for (; j + 2 < n_full; j += 2) {
     body(j, std::false_type{}, std::true_type{}, s_a, s_b);
     body(j + 1, std::false_type{}, std::true_type{}, s_b, s_a);
@@ -310,18 +329,19 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN = false>
 static hipError_t launch_fwd(FwdArgs a, hipStream_t stream) {
   using C = FwdCfg<D>;
   a.n_qtiles = (a.Tq + C::BR - 1) / C::BR;
   const uint32_t n = (uint32_t)a.n_qtiles * (uint32_t)(a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WIN>), dim3(n), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
 int fwd_rows_per_workgroup(int d) { return d == 128 ? FwdCfg<128>::BR : FwdCfg<64>::BR; }
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
+  if (a.window > 0) return d == 64 ? launch_fwd<64, true, true>(a, stream) : launch_fwd<128, true, true>(a, stream);
   if (d == 64) return causal ? launch_fwd<64, true>(a, stream) : launch_fwd<64, false>(a, stream);
   return causal ? launch_fwd<128, true>(a, stream) : launch_fwd<128, false>(a, stream);
 }

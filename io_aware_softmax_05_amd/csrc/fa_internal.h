@@ -17,6 +17,7 @@ struct FwdArgs {
   int B, Hq, Hkv, Tq, Tk;
   float c;            // scale * log2(e)
   int n_qtiles;       // filled in by the launcher
+  int window;         // causal band of this many keys (0: plain mask)
 };
 
 struct FwdF32Args {
@@ -43,6 +44,7 @@ struct DecodeArgs {
   int chunk;                // keys per split (multiple of 64)
   int n_splits;             // ceil(Tk_max / chunk)
   float c;                  // scale * log2(e)
+  int window;               // only the last `window` keys are seen (0: all)
 };
 
 struct BwdArgs {
@@ -59,6 +61,7 @@ struct BwdArgs {
   int B, Hq, Hkv, Tq, Tk;
   float scale;
   float c;                  // scale * log2(e)
+  int window;               // causal band of this many keys (0: plain mask)
 };
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);

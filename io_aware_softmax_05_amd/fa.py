@@ -38,11 +38,14 @@ _S = ctypes.c_size_t
 _SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_decode_splitkv_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
 }
 
 _lib = None
@@ -124,6 +127,12 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream=None) -
     _check(st, "fa_fwd")
 
 
+def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, window, stream=None) -> None:
+    st = load_library().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
+                                      float(scale), int(window), _stream(stream))
+    _check(st, "fa_fwd_window")
+
+
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream=None) -> None:
     st = load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
                                    float(scale), int(bool(causal)), _stream(stream))
@@ -142,6 +151,14 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, T
     _check(st, "fa_bwd")
 
 
+def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, window,
+                  stream=None) -> None:
+    st = load_library().fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tq, Tk, d,
+                                      float(scale), int(window), _stream(stream))
+    _check(st, "fa_bwd_window")
+
+
 def fa_decode_workspace_size(B, Hq, Tk_max, d) -> int:
     return int(load_library().fa_decode_workspace_size(B, Hq, Tk_max, d))
 
@@ -152,6 +169,14 @@ def fa_decode_splitkv(q, k_cache, v_cache, seq_lens, o, lse, workspace, ws_bytes
                                           _ptr(lse), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tk_max, d,
                                           float(scale), int(chunk), _stream(stream))
     _check(st, "fa_decode_splitkv")
+
+
+def fa_decode_splitkv_window(q, k_cache, v_cache, seq_lens, o, lse, workspace, ws_bytes, B, Hq, Hkv, Tk_max, d,
+                             scale, window, chunk=0, stream=None) -> None:
+    st = load_library().fa_decode_splitkv_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(o),
+                                                 _ptr(lse), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tk_max,
+                                                 d, float(scale), int(window), int(chunk), _stream(stream))
+    _check(st, "fa_decode_splitkv_window")
 
 
 # ------------------------------------------------ tensor-level conveniences

@@ -145,3 +145,26 @@ def test_binding_raises_on_error():
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, A, A, A, None, 1, 1, 1, 4, 4, 48, 0.1, False, stream=0)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ sliding window
+
+@pytest.mark.parametrize("window", [0, -1, -4096])
+def test_window_entry_points_reject_empty_windows(window):
+    L = lib()
+    assert L.fa_fwd_window(A, A, A, A, None, 1, 2, 1, 8, 8, 64, 0.125, window, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_window(A, A, A, A, A, A, A, A, A, A, 1 << 20, 1, 2, 1, 8, 8, 64, 0.125, window,
+                           None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_decode_splitkv_window(A, A, A, A, A, None, A, 1 << 30, 2, 8, 2, 256, 128, 0.1, window, 0,
+                                      None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_window_entry_points_check_like_the_plain_ones():
+    L = lib()
+    # the same argument checks run first: d, Hq % Hkv, NULL outputs, workspace
+    assert L.fa_fwd_window(A, A, A, A, None, 1, 2, 1, 8, 8, 48, 0.125, 4, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_fwd_window(A, A, A, None, None, 1, 2, 1, 8, 8, 64, 0.125, 4, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_window(A, A, A, A, A, A, A, A, A, None, 1 << 20, 1, 2, 1, 8, 8, 64, 0.125, 4,
+                           None) == fa.FA_ERR_WORKSPACE
+    assert L.fa_decode_splitkv_window(A, A, A, A, A, None, A, 1 << 30, 2, 6, 4, 256, 128, 0.1, 4, 0,
+                                      None) == fa.FA_ERR_INVALID_ARG

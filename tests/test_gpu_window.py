@@ -1,0 +1,126 @@
+"""GPU parity of the causal sliding-window entry points (fa_fwd_window,
+fa_bwd_window, fa_decode_splitkv_window) against the fp64 oracle's band."""
+import numpy as np
+import pytest
+import torch
+
+from io_aware_softmax_05_amd import fa, inputs
+from oracle import attention_ref as ref
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd_window(dev, scale, window):
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, window)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+WIN_SHAPES = [
+    # B, Hq, Hkv, Tq, Tk, d, window
+    (1, 2, 2, 300, 300, 128, 16),      # window inside one 64-key tile
+    (1, 2, 2, 300, 300, 128, 64),
+    (1, 4, 2, 600, 600, 128, 200),     # several tiles, head tiles masked per row
+    (1, 2, 1, 257, 257, 64, 100),
+    (2, 4, 4, 130, 130, 64, 1),        # each row sees only its own key
+    (1, 4, 1, 100, 300, 128, 77),      # Tq < Tk (bottom-right band)
+    (1, 2, 2, 150, 90, 64, 40),        # Tq > Tk: the first 60 rows see no key
+    (1, 6, 2, 333, 333, 128, 129),     # 3 query heads per KV head
+]
+
+
+@pytest.mark.parametrize("shape", WIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_window_forward_parity(shape):
+    B, Hq, Hkv, Tq, Tk, d, w = shape
+    print(f"[fwd window {shape}]", flush=True)
+    hv, dev = gu.attention_case(500 + Tq + w, B, Hq, Hkv, Tq, Tk, d)
+    scale = d ** -0.5
+    o, lse = _fwd_window(dev, scale, w)
+    o_r, lse_r = ref.attention_fwd(hv["q"], hv["k"], hv["v"], scale, True, window=w)
+    gu.check_bf16("O", o, o_r)
+    gu.check_lse("LSE", lse, lse_r, 1e-4)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_as_long_as_the_sequence_is_the_causal_kernel(d):
+    """A window covering every row's keys computes exactly what the causal
+    forward computes (same tiles, same arithmetic): bit-identical outputs."""
+    hv, dev = gu.attention_case(77, 1, 4, 2, 520, 520, d)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    o1, l1 = _fwd_window(dev, d ** -0.5, 520)
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(l1)
+    fa.fa_fwd(q, k, v, o2, l2, 1, 4, 2, 520, 520, d, d ** -0.5, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+BWD_WIN_SHAPES = [
+    (1, 2, 2, 300, 300, 64, 50),
+    (1, 4, 2, 400, 400, 128, 130),
+    (1, 2, 2, 257, 257, 128, 1),
+    (1, 4, 1, 120, 260, 64, 90),       # Tq < Tk, 4 query heads per KV head
+    (1, 2, 2, 600, 600, 64, 300),      # windows spanning several 256-key workgroups
+]
+
+
+@pytest.mark.parametrize("shape", BWD_WIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_window_backward_parity(shape):
+    B, Hq, Hkv, Tq, Tk, d, w = shape
+    print(f"[bwd window {shape}]", flush=True)
+    hv, dev = gu.attention_case(700 + Tq + w, B, Hq, Hkv, Tq, Tk, d, with_dout=True)
+    scale = d ** -0.5
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = _fwd_window(dev, scale, w)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Tq, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    fa.fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, w)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = ref.attention_bwd(hv["q"], hv["k"], hv["v"], hv["do"], scale, True, window=w)
+    gu.check_bf16("dQ", dq, dq_r)
+    gu.check_bf16("dK", dk, dk_r)
+    gu.check_bf16("dV", dv, dv_r)
+
+
+@pytest.mark.parametrize("shape", [(3, 8, 2, 600, 128, 1, 600, 100, 0), (2, 4, 4, 1000, 64, 1, 1000, 333, 64),
+                                   (4, 32, 8, 700, 128, 60, 700, 64, 128), (2, 8, 2, 300, 128, 1, 300, 1000, 0),
+                                   (2, 8, 2, 500, 128, 1, 500, 1, 0)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_window_decode_parity(shape):
+    B, Hq, Hkv, Tk_max, d, lo, hi, w, chunk = shape
+    print(f"[decode window {shape}]", flush=True)
+    raw = inputs.draw_decode_inputs(900 + w, B, Hq, Hkv, Tk_max, d, lo=lo, hi=hi)
+    dev = {n: gu.dev_bf16(raw[n]) for n in ("q", "k", "v")}
+    lens = torch.from_numpy(raw["seq_lens"]).cuda()
+    ws_bytes = fa.fa_decode_workspace_size(B, Hq, Tk_max, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    scale = d ** -0.5
+    fa.fa_decode_splitkv_window(dev["q"], dev["k"], dev["v"], lens, o, lse, ws, ws_bytes, B, Hq, Hkv, Tk_max, d,
+                                scale, w, chunk)
+    torch.cuda.synchronize()
+    hv = {n: inputs.widen(raw[n]) for n in ("q", "k", "v")}
+    o_r, lse_r = ref.decode(hv["q"], hv["k"], hv["v"], raw["seq_lens"], scale, window=w)
+    gu.check_bf16("O", o, o_r)
+    gu.check_lse("LSE", lse, lse_r, 1e-4)
+
+
+def test_window_long_sequence_sampled_rows():
+    """A 4096-key sequence with a 1024-key window (rows sampled for the oracle)."""
+    B, Hq, Hkv, T, d, w = 1, 4, 1, 4096, 128, 1024
+    hv, dev = gu.attention_case(4242, B, Hq, Hkv, T, T, d)
+    scale = d ** -0.5
+    o, lse = _fwd_window(dev, scale, w)
+    rows = np.unique(np.concatenate([np.arange(0, 5), np.arange(1020, 1030), np.arange(T - 5, T),
+                                     np.random.Generator(np.random.PCG64(3)).integers(0, T, 40)]))
+    o_r, lse_r = ref.attention_fwd(hv["q"], hv["k"], hv["v"], scale, True, rows=rows, window=w)
+    gu.check_bf16("O (sampled rows)", gu.host(o)[:, :, rows], o_r)
+    gu.check_lse("LSE (sampled rows)", gu.host(lse)[:, :, rows], lse_r, 1e-4)
