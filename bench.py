@@ -222,6 +222,49 @@ def run_decode(steps, warmup):
             "sum_lengths": int(lens_np.sum())}
 
 
+def window_pairs(T, W):
+    """Visible (query, key) pairs of a square causal band of W keys."""
+    W = min(W, T)
+    return W * T - W * (W - 1) // 2
+
+
+def run_window(steps, warmup):
+    """Causal sliding-window layer fwd + bwd: B1 Hq32 Hkv8 T32768 d128, W = 4096."""
+    import torch
+    from io_aware_softmax_05_amd import fa
+    B, Hq, Hkv, T, d, W = 1, 32, 8, 32768, 128, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    q = _randn_bf16((B, Hq, T, d), gen)
+    k = _randn_bf16((B, Hkv, T, d), gen)
+    v = _randn_bf16((B, Hkv, T, d), gen)
+    do = _randn_bf16((B, Hq, T, d), gen)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_size(B, Hq, T, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    t_f, t_b = Timer(stream), Timer(stream)
+
+    def f():
+        fa.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, T, T, d, d ** -0.5, W, stream)
+
+    def b():
+        fa.fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, d ** -0.5, W, stream)
+
+    for _ in range(warmup):
+        f()
+        b()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        t_f.record(f)
+        t_b.record(b)
+    torch.cuda.synchronize()
+    ff = 4.0 * d * window_pairs(T, W) * B * Hq
+    return {"fwd_ms": t_f.median_ms(), "bwd_ms": t_b.median_ms(), "fwd_flop": ff, "bwd_flop": 2.5 * ff}
+
+
 def run_small_f32(steps, warmup):
     """The single-head fp32 workload (B1 H1 T256 d64): latency only."""
     import torch
@@ -451,6 +494,12 @@ def main():
             "mfma", g32["fwd_flop"], g32["fwd_ms"], "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128")
         out["targets"]["fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128"] = roofline(
             "mfma", g32["bwd_flop"], g32["bwd_ms"], "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128")
+        torch.cuda.empty_cache()
+        sw = run_window(5, 2)
+        out["targets"]["fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128"] = roofline(
+            "mfma", sw["fwd_flop"], sw["fwd_ms"], "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128")
+        out["targets"]["fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128"] = roofline(
+            "mfma", sw["bwd_flop"], sw["bwd_ms"], "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128")
         f32 = run_small_f32(50, 10)
         out["latency"] = {"fa_fwd_f32 B1 H1 T256 d64": {"median_us": round(f32["median_ms"] * 1e3, 2),
                                                         "flop": f32["flop"], "bound": "latency"}}

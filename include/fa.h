@@ -66,8 +66,9 @@ const char* fa_status_string(int status);
  *   q [B,Hq,Tq,d], k and v [B,Hkv,Tk,d]  (bf16, read only)
  *   o [B,Hq,Tq,d]                        (bf16, written)
  *   lse [B,Hq,Tq] fp32, written when non-NULL; it is what fa_bwd needs to
- *   recompute the probabilities (aimlrounds "FlashAttention": one fp32
- *   log-sum-exp per row and head is kept for the backward pass).
+ *   recompute the probabilities (aimlrounds "FlashAttention": the forward
+ *   keeps a single fp32 log-sum-exp for each row of each head, for the
+ *   backward pass).
  * QK^T and PV run on bf16 matrix cores; the probabilities are rounded to bf16
  * before the PV product, the running sum uses them unrounded.
  * Errors: FA_ERR_INVALID_ARG (q/k/v/o NULL, any size <= 0, Hq % Hkv != 0,

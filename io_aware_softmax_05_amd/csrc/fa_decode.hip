@@ -4,8 +4,8 @@
 // aimlrounds "FlashAttention", note under the "FlashAttention 1, 2, 3" table:
 // with a single query token the long KV cache is split across workgroups.
 // zerotofrontier "Efficient attention: memory-bound", section "Every kernel
-// is below the ridge": decoding does about one FLOP per cached byte, so the
-// time is set by how fast the cache streams out of HBM.
+// is below the ridge": decoding does about one FLOP per cached byte, so its
+// run time follows the rate at which HBM delivers the cache.
 //
 // Kernel 1 (split). Work items are (batch, KV head, query-row group, chunk)
 // for the chunks that hold cached keys; the item list is dense (chunks past a

@@ -110,7 +110,7 @@ def test_online_rescale_applies_to_both_sums():
 @pytest.mark.parametrize("shape", [(17, 17), (9, 23), (23, 9), (1, 30)])
 def test_tile_size_invariance(causal, shape):
     """The recurrence at any tile size equals the three-step oracle
-    (aimlrounds page: every tile size gives the same answer up to rounding)."""
+    (aimlrounds page: the result does not depend on the tile size, up to rounding)."""
     Tq, Tk = shape
     rng = np.random.Generator(np.random.PCG64(Tq * 100 + Tk))
     q = rng.standard_normal((Tq, 5)) * 2.0
