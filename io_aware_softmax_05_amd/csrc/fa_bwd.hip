@@ -214,8 +214,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
           const int r = 4 * g4 + e;
           float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
           if constexpr (decltype(masked)::value) {
-            const int lim = q0 + rq + e + shift;
-            if (key > lim || (WIN && key <= lim - a.window)) pe = 0.f;
+            // visible iff 0 <= (row + shift) - key < window (one unsigned compare)
+            const int dist = q0 + rq + e + shift - key;
+            if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
           }
           p[e] = pe;
           ds[e] = pe * (dp[qb][r] - dl[e]);
