@@ -198,6 +198,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
       }
     }
     // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
+    // Masked tiles: row q0 + 32 qb + 8 g4 + 4 half + e sees this lane's key iff
+    // 0 <= dist < window with dist = (that row + shift - key) = dbase + 32 qb + 8 g4 + e.
+    const int dbase = q0 + 4 * half + shift - key;
     uint32_t pw[QB][8], dsw[QB][8];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -214,8 +217,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
           const int r = 4 * g4 + e;
           float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
           if constexpr (decltype(masked)::value) {
-            // visible iff 0 <= (row + shift) - key < window (one unsigned compare)
-            const int dist = q0 + rq + e + shift - key;
+            const int dist = dbase + (qb * 32 + 8 * g4 + e);   // one unsigned compare for the band
             if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
           }
           p[e] = pe;
@@ -226,7 +228,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
         dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
         dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
       }
-    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
+    // (the hint on the unmasked body only: on the masked one it costs registers)
+    if constexpr (C::IGLP >= 0 && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(C::IGLP);
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -521,8 +524,11 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
                      a, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_ktiles = (a.Tk + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DkdvCfg<D>, WIN>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(DkdvCfg<D>::NT), 0, stream,
+  // masked d = 64 tiles: 32-row query tiles (the 64-row masked body spills at
+  // two waves per SIMD; measured 27% faster on a causal T2048 layer)
+  using KC = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>, DkdvCfg<D>>::type;
+  const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0, stream,
                      a, n_ktiles);
   return hipGetLastError();
 }
