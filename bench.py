@@ -71,13 +71,15 @@ DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
 # Launch units whose HBM traffic is recorded: unit -> kernel names (prefix of
 # the demangled name, up to the argument list).
 TRAFFIC_UNITS = {
-    "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false>"],
-    "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false>", "bwd_dkdv_kernel<64, false>"],
+    "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false, false>"],
+    "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false, false>", "bwd_dkdv_kernel<64, false, false>"],
     # the causal 8k and 32k forwards run the same kernel: told apart by grid size (threads)
-    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true>@524288"],
-    "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128", "decode_merge_kernel<128>"],
-    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true>@2097152"],
-    "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true>", "bwd_dkdv_kernel<128, true>"],
+    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true, false>@524288"],
+    "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128, 3>", "decode_merge_kernel<128>"],
+    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false>@2097152"],
+    "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false>", "bwd_dkdv_kernel<128, true, false>"],
+    "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true>"],
+    "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["bwd_dq_kernel<128, true, true>", "bwd_dkdv_kernel<128, true, true>"],
 }
 
 
@@ -349,6 +351,29 @@ def cpu_baseline(res, seconds):
 
 # ----------------------------------------------------------- counter records
 
+def kernel_key(name: str) -> str:
+    """'void fa::k<128, true, fa::Cfg<128, 4>, true>(fa::Args)' -> 'k<128, true, true>':
+    the template arguments that pick the variant, without tuning-config structs."""
+    base = name[len("void fa::"):] if name.startswith("void fa::") else name
+    head, lt, rest = base.partition("<")
+    if not lt:
+        return base.split("(")[0]
+    args, depth, cur = [], 0, ""
+    for ch in rest:
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            if depth == 0:
+                break
+            depth -= 1
+        if ch == "," and depth == 0:
+            args.append(cur.strip()); cur = ""
+        else:
+            cur += ch
+    args.append(cur.strip())
+    return head + "<" + ", ".join(a for a in args if not a.startswith("fa::")) + ">"
+
+
 def _counter_means(path, counter):
     """Mean per-dispatch value of `counter` for each fa:: kernel (and the
     runtime's copy kernel) in one rocprofv3 counter_collection.csv."""
@@ -359,9 +384,7 @@ def _counter_means(path, counter):
                 continue
             name = r["Kernel_Name"]
             if name.startswith("void fa::"):
-                key = name[len("void fa::"):].split("(")[0]
-                if ", fa::" in key:   # drop a tuning-config template argument
-                    key = key.split(", fa::")[0] + ">"
+                key = kernel_key(name)
             elif "copyBuffer" in name:
                 key = "copy"
             else:
@@ -390,7 +413,7 @@ def record_traffic(d):
         total = 0.0
         for spec in kernels:
             k, _, grid = spec.partition("@")
-            hits = [nk for nk in fetch if nk[0].startswith(k) and (not grid or nk[1] == int(grid))]
+            hits = [nk for nk in fetch if nk[0] == k and (not grid or nk[1] == int(grid))]
             if len(hits) != 1:
                 raise SystemExit(f"{len(hits)} counter records match kernel {spec}: {hits}")
             nk = hits[0]
