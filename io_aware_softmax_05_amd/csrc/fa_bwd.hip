@@ -341,12 +341,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
+  // Tile order: (batch, kv head) outermost, then query tile, then the query
+  // heads that share the kv head, so the workgroups that run together on an
+  // XCD read the same K/V tiles at about the same time.
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt_lin = (int)(t % (uint32_t)n_qtiles);
-  const int bh = (int)(t / (uint32_t)n_qtiles);
+  const uint32_t G = (uint32_t)(a.Hq / a.Hkv), per_grp = (uint32_t)n_qtiles * G;
+  const uint32_t kvg = t / per_grp, r = t - kvg * per_grp;
+  const int qt_lin = (int)(r / G), g = (int)(r - (uint32_t)qt_lin * G);
   const int qt = CAUSAL ? (n_qtiles - 1 - qt_lin) : qt_lin;
-  const int b = bh / a.Hq, h = bh - b * a.Hq;
-  const int hk = h / (a.Hq / a.Hkv);
+  const int b = (int)kvg / a.Hkv, hk = (int)kvg - b * a.Hkv;
+  const int h = hk * (int)G + g, bh = b * a.Hq + h;
   const int q0 = qt * C::BR;
   const int qw0 = q0 + wave * 32;                 // first row of this wave
   const int qrow = qw0 + col;                     // this lane's query row

@@ -12,7 +12,8 @@
 // gfx950 mapping
 //   * workgroup = NW waves x 32 query rows (NW = 8 at d = 128, 4 at d = 64);
 //     grid = query tiles x heads x batch, remapped so that the tiles of one
-//     head share an XCD (and its L2), causal tiles longest first.
+//     kv head (all query heads that share it) run on one XCD and its L2,
+//     query heads of a group side by side, causal tiles longest first.
 //   * 64-key K and V tiles stream HBM -> registers -> LDS through buffer
 //     loads (out-of-range rows read as zeros, so the loop has no branches),
 //     double buffered with one barrier per tile. Row pitches are chosen for
@@ -82,12 +83,16 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   const int half = lane >> 5;             // which 16-key half of a 32-key block
   const int col = lane & 31;              // query column owned by this lane
 
+  // Tile order: (batch, kv head) outermost, then query tile, then the query
+  // heads that share the kv head, so the workgroups that run together on an
+  // XCD read the same K/V tiles at about the same time.
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt_lin = (int)(t % (uint32_t)a.n_qtiles);
-  const int bh = (int)(t / (uint32_t)a.n_qtiles);
+  const uint32_t G = (uint32_t)(a.Hq / a.Hkv), per_grp = (uint32_t)a.n_qtiles * G;
+  const uint32_t kvg = t / per_grp, r = t - kvg * per_grp;
+  const int qt_lin = (int)(r / G), g = (int)(r - (uint32_t)qt_lin * G);
   const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_lin) : qt_lin;
-  const int b = bh / a.Hq, h = bh - b * a.Hq;
-  const int hk = h / (a.Hq / a.Hkv);
+  const int b = (int)kvg / a.Hkv, hk = (int)kvg - b * a.Hkv;
+  const int h = hk * (int)G + g, bh = b * a.Hq + h;
   const int q0 = qt * BR;
   const size_t qoff = (size_t)bh * a.Tq * D;
   const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
