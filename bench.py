@@ -199,8 +199,9 @@ def run_decode(steps, warmup):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(DECODE["seed"])
     q = _randn_bf16((B, Hq, d), gen)
-    kc = _randn_bf16((B, Hkv, Tk_max, d), gen)   # 1 GiB each: far larger than the 256 MiB MALL
-    vc = _randn_bf16((B, Hkv, Tk_max, d), gen)
+    # two cache copies (1 GiB per tensor each), used in turn, so that no call
+    # finds the previous call's rows in the 256 MiB MALL
+    caches = [(_randn_bf16((B, Hkv, Tk_max, d), gen), _randn_bf16((B, Hkv, Tk_max, d), gen)) for _ in range(2)]
     lens = torch.from_numpy(lens_np).cuda()
     ws_bytes = fa.fa_decode_workspace_size(B, Hq, Tk_max, d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -209,7 +210,11 @@ def run_decode(steps, warmup):
     stream = torch.cuda.current_stream()
     t = Timer(stream)
 
+    turn = [0]
+
     def call():
+        kc, vc = caches[turn[0] & 1]
+        turn[0] += 1
         fa.fa_decode_splitkv(q, kc, vc, lens, o, lse, ws, ws_bytes, B, Hq, Hkv, Tk_max, d, d ** -0.5, 0, stream)
 
     for _ in range(warmup):
