@@ -103,6 +103,32 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                hipStream_t stream);
 
 /*
+ * Forward pass on fp8 inputs (OCP e4m3 bytes), bf16 output, fp32 log-sum-exp.
+ * The aimlrounds "FlashAttention" page (table "FlashAttention 1, 2, 3") lists
+ * FP8 among the FlashAttention-3 changes without a recipe; this is the one
+ * taken:
+ *   q [B,Hq,Tq,d] and k [B,Hkv,Tk,d]  e4m3 bytes, row-major (read only)
+ *   vt [B,Hkv,d,Tk]                   e4m3 bytes of V, TRANSPOSED (read only)
+ *   q_scale [B*Hq], k_scale [B*Hkv], v_scale [B*Hkv]  fp32 device arrays:
+ *                                     the value of a byte x of head (b, h) is
+ *                                     x * scale[b*H + h]
+ *   o [B,Hq,Tq,d] bf16 and lse [B,Hq,Tq] fp32 (written; lse may be NULL)
+ * Computes softmax(scale * Q K^T (+ causal mask)) V on the dequantised values.
+ * QK^T and PV run on fp8 matrix cores with fp32 accumulation; the
+ * probabilities (times 2^6, at most 2^8) are rounded to e4m3 before the PV
+ * product, the running sum uses them unrounded, so O carries a relative error
+ * of up to 2^-4 per probability, LSE only the score rounding.
+ * Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for NULL vt/q_scale/k_scale/
+ * v_scale and for Tk not a multiple of 16 (the V^T rows are read in 16-byte
+ * chunks); every pointer must be 16-byte aligned except the scale arrays
+ * (4-byte).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* vt,
+               const float* q_scale, const float* k_scale, const float* v_scale,
+               void* o, float* lse, int B, int Hq, int Hkv, int Tq, int Tk, int d,
+               float scale, int causal, hipStream_t stream);
+
+/*
  * Workspace bytes fa_bwd needs: two fp32 per query row, the row's LSE in
  * base-2 units and D_i = sum_c dO_ic O_ic, rounded up to 256 bytes. Linear in
  * Tq, never quadratic (aimlrounds "FlashAttention": the N x N matrix is not

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfa_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -73,6 +73,35 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, 0, stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* vt,
+               const float* q_scale, const float* k_scale, const float* v_scale,
+               void* o, float* lse, int B, int Hq, int Hkv, int Tq, int Tk, int d,
+               float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !vt || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_INVALID_ARG;
+  const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
+  if (st != FA_OK) return st;
+  if (Tk % 16 != 0) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+       reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+    return FA_ERR_INVALID_ARG;
+  const int br = fa::fwd_fp8_rows_per_workgroup(d);
+  if ((int64_t)((Tq + br - 1) / br) * B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  fa::Fp8Args a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.vt = static_cast<const uint8_t*>(vt);
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.c = scale * fa::kLog2eHost;
+  return to_status(fa::launch_fwd_fp8(a, d, causal != 0, stream));
+}
+
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int window,
                   hipStream_t stream) {

@@ -20,6 +20,20 @@ struct FwdArgs {
   int window;         // causal band of this many keys (0: plain mask)
 };
 
+struct Fp8Args {
+  const uint8_t* q;         // [B,Hq,Tq,d] e4m3
+  const uint8_t* k;         // [B,Hkv,Tk,d] e4m3
+  const uint8_t* vt;        // [B,Hkv,d,Tk] e4m3 (V transposed)
+  const float* q_scale;     // [B,Hq]  value = byte * scale
+  const float* k_scale;     // [B,Hkv]
+  const float* v_scale;     // [B,Hkv]
+  uint16_t* o;              // [B,Hq,Tq,d] bf16
+  float* lse;               // [B,Hq,Tq] or null
+  int B, Hq, Hkv, Tq, Tk;
+  float c;                  // scale * log2(e)
+  int n_qtiles;             // filled in by the launcher
+};
+
 struct FwdF32Args {
   const float* q;
   const float* k;
@@ -67,6 +81,8 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
 int fwd_rows_per_workgroup(int d);
 hipError_t launch_fwd_f32(FwdF32Args a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(Fp8Args a, int d, bool causal, hipStream_t stream);
+int fwd_fp8_rows_per_workgroup(int d);
 hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream);
 

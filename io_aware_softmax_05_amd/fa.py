@@ -40,6 +40,7 @@ _SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -137,6 +138,14 @@ def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream=Non
     st = load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
                                    float(scale), int(bool(causal)), _stream(stream))
     _check(st, "fa_fwd_f32")
+
+
+def fa_fwd_fp8(q, k, vt, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal,
+               stream=None) -> None:
+    st = load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(vt), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                   _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)),
+                                   _stream(stream))
+    _check(st, "fa_fwd_fp8")
 
 
 def fa_bwd_workspace_size(B, Hq, Tq, d) -> int:

@@ -2,7 +2,8 @@
 and benchmark and by the CPU oracle's tests.
 
 This module only draws random numbers and rounds them to the storage types the
-kernels consume (fp32, bf16). It holds none of the attention arithmetic.
+kernels consume (fp32, bf16, and e4m3 bytes with per-head factors). It holds
+none of the attention arithmetic.
 
 Recipe (one PCG64 stream per workload, seeded with the workload's number):
   * draw order: [seq_lens], Q, K, V, dO -- each tensor is drawn in full, in
@@ -10,7 +11,10 @@ Recipe (one PCG64 stream per workload, seeded with the workload's number):
   * values: standard normal in fp64, rounded to fp32 (round to nearest even),
     then, for bf16 workloads, rounded to bf16 (round to nearest even, done on
     the fp32 bit pattern);
-  * decode lengths: integers uniform on [4096, 32768], both ends included.
+  * decode lengths: integers uniform on [4096, 32768], both ends included;
+  * fp8 workloads: Q, K, V drawn as fp32, then each (batch, head) divided by
+    max|x| / 448 and rounded to e4m3 (nearest, ties to even); V is handed
+    over transposed, [B, Hkv, d, Tk].
 Both sides consume the rounded values: the GPU gets the bit patterns, the
 oracle gets the same numbers widened to fp64.
 """
@@ -69,6 +73,58 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
         e = min(n, s + _CHUNK)
         out[s:e] = bf16_bits_from_f32(rng.standard_normal(e - s).astype(np.float32))
     return out.reshape(shape)
+
+
+def _e4m3_positive_grid() -> np.ndarray:
+    """The 127 non-negative finite OCP E4M3 values, indexed by their code 0x00..0x7E."""
+    codes = np.arange(127)
+    e, f = codes >> 3, codes & 7
+    return np.where(e == 0, f * 2.0 ** -9, (8 + f) * np.exp2(e - 10.0))
+
+
+_E4M3_GRID = _e4m3_positive_grid()
+
+
+def e4m3_bits_from_f64(x: np.ndarray) -> np.ndarray:
+    """Round values with |x| <= 448 to OCP E4M3 bytes, nearest, ties to the even code."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if not np.all(a <= 448.0):
+        raise ValueError("e4m3 input out of range (|x| <= 448)")
+    hi = np.clip(np.searchsorted(_E4M3_GRID, a, side="left"), 1, 126)
+    lo = hi - 1
+    d_lo, d_hi = a - _E4M3_GRID[lo], _E4M3_GRID[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == 0.0, 0, code)
+    return (code | np.where(np.signbit(x) & (code != 0), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3_per_head(x: np.ndarray):
+    """x [B,H,T,d] -> (e4m3 bytes [B,H,T,d], fp32 factors [B,H]): each (batch, head)
+    is divided by max|x| / 448 (its largest magnitude lands on 448) and rounded."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=(2, 3))
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    y = x / scale.astype(np.float64)[:, :, None, None]
+    return e4m3_bits_from_f64(np.clip(y, -448.0, 448.0)), scale
+
+
+def draw_fp8_attention_inputs(seed: int, B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int) -> dict:
+    """fp8 forward inputs: Q, K, V drawn as for fp32 (N(0,1) -> fp32), then
+    quantised per (batch, head) to e4m3; V is handed over transposed.
+
+    Returns q8 [B,Hq,Tq,d], k8 [B,Hkv,Tk,d], vt8 [B,Hkv,d,Tk] (uint8) and
+    q_scale [B,Hq], k_scale, v_scale [B,Hkv] (fp32)."""
+    rng = make_rng(seed)
+    q = normal_f32(rng, (B, Hq, Tq, d))
+    k = normal_f32(rng, (B, Hkv, Tk, d))
+    v = normal_f32(rng, (B, Hkv, Tk, d))
+    q8, qs = quantize_e4m3_per_head(q)
+    k8, ks = quantize_e4m3_per_head(k)
+    v8, vs = quantize_e4m3_per_head(v)
+    return {"q8": q8, "k8": k8, "vt8": np.ascontiguousarray(np.swapaxes(v8, 2, 3)),
+            "q_scale": qs, "k_scale": ks, "v_scale": vs}
 
 
 def decode_lengths(rng: np.random.Generator, batch: int, lo: int = 4096, hi: int = 32768) -> np.ndarray:

@@ -111,6 +111,38 @@ def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, window: int = 
     return o, lse
 
 
+def e4m3_to_f64(bits) -> np.ndarray:
+    """Values of OCP 8-bit floats in the E4M3 format, exactly, as fp64.
+
+    E4M3 (the variant without infinities): 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits. Exponent field 0 holds the subnormals
+    (mantissa / 8) * 2^-6; the codes S.1111.111 are NaN; every other code is
+    (1 + mantissa / 8) * 2^(exponent - 7), the largest being 448."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where((b >> 7) != 0, -1.0, 1.0)
+    e = (b >> 3) & 15
+    f = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, (f / 8.0) * 2.0 ** -6, (1.0 + f / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (f == 7), np.nan, mag)
+    return sign * mag
+
+
+def attention_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, scale: float, causal: bool, rows=None):
+    """Forward on fp8 inputs: exact attention over the values the bytes stand for.
+
+    aimlrounds "FlashAttention", table "FlashAttention 1, 2, 3", lists FP8
+    among the FlashAttention-3 changes and gives no recipe; the reading taken
+    is per-(batch, head) dequantisation factors:
+      q8 [B,Hq,Tq,d], k8 [B,Hkv,Tk,d] e4m3 bytes; vt8 [B,Hkv,d,Tk] e4m3 bytes
+      of V transposed; q_scale [B,Hq], k_scale and v_scale [B,Hkv];
+      Q = e4m3(q8) * q_scale[b, h] (likewise K and V per kv head).
+    Returns O and LSE of softmax(scale Q K^T [+causal]) V, as attention_fwd."""
+    q = e4m3_to_f64(q8) * np.asarray(q_scale, dtype=np.float64)[:, :, None, None]
+    k = e4m3_to_f64(k8) * np.asarray(k_scale, dtype=np.float64)[:, :, None, None]
+    v = np.swapaxes(e4m3_to_f64(vt8), 2, 3) * np.asarray(v_scale, dtype=np.float64)[:, :, None, None]
+    return attention_fwd(q, k, v, scale, causal, rows)
+
+
 def attention_bwd(q, k, v, do, scale: float, causal: bool, window: int = 0):
     """Backward of O = softmax(scale Q K^T [+mask]) V given dO.
 

@@ -168,3 +168,24 @@ def test_window_entry_points_check_like_the_plain_ones():
                            None) == fa.FA_ERR_WORKSPACE
     assert L.fa_decode_splitkv_window(A, A, A, A, A, None, A, 1 << 30, 2, 6, 4, 256, 128, 0.1, 4, 0,
                                       None) == fa.FA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ fp8 forward
+
+def test_fp8_forward_rejects_bad_arguments():
+    L = lib()
+    S = 0x10004   # a 4-byte aligned (not 16-byte aligned) address for the scale arrays
+    ok = (A, A, A, S, S, S, A, None, 1, 2, 1, 8, 32, 64, 0.125, 1, None)
+    bad = {
+        "Tk not a multiple of 16": (A, A, A, S, S, S, A, None, 1, 2, 1, 8, 40, 64, 0.125, 1, None),
+        "NULL vt": (A, A, None, S, S, S, A, None, 1, 2, 1, 8, 32, 64, 0.125, 1, None),
+        "NULL q_scale": (A, A, A, None, S, S, A, None, 1, 2, 1, 8, 32, 64, 0.125, 1, None),
+        "NULL v_scale": (A, A, A, S, S, None, A, None, 1, 2, 1, 8, 32, 64, 0.125, 1, None),
+        "misaligned scale": (A, A, A, S + 2, S, S, A, None, 1, 2, 1, 8, 32, 64, 0.125, 1, None),
+        "misaligned vt": (A, A, A + 8, S, S, S, A, None, 1, 2, 1, 8, 32, 64, 0.125, 1, None),
+        "Hq % Hkv": (A, A, A, S, S, S, A, None, 1, 3, 2, 8, 32, 64, 0.125, 1, None),
+        "zero scale": (A, A, A, S, S, S, A, None, 1, 2, 1, 8, 32, 64, 0.0, 1, None),
+    }
+    for name, args in bad.items():
+        assert L.fa_fwd_fp8(*args) == fa.FA_ERR_INVALID_ARG, name
+    assert L.fa_fwd_fp8(*ok[:13], 48, *ok[14:]) == fa.FA_ERR_UNSUPPORTED   # d

@@ -1,0 +1,149 @@
+"""Pins for the oracle's fp8 forward and the fp8 input recipe.
+
+The pages name FP8 as a FlashAttention-3 change (aimlrounds "FlashAttention",
+table "FlashAttention 1, 2, 3") and give no format or scaling recipe. The
+readings taken: OCP E4M3 bytes (no infinities, largest value 448), one fp32
+factor per (batch, head), V handed over transposed. The decoder is pinned to
+the format's fixed points written as literals (not to its own formula); the
+dequantisation and the V orientation to closed forms of attention on chosen
+bytes; the per-head factors to heads that must not feel each other's factor.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+from io_aware_softmax_05_amd import inputs
+from oracle import attention_ref as ref
+
+
+# ---------------------------------------------------------------- the decoder
+
+E4M3_FIXED_POINTS = {
+    0x00: 0.0, 0x01: 2.0 ** -9, 0x02: 2.0 ** -8, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x09: 1.125 * 2.0 ** -6,
+    0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x48: 4.0, 0x4F: 7.5, 0x77: 240.0, 0x78: 256.0,
+    0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xC2: -2.5, 0xFE: -448.0,
+}
+
+
+def test_e4m3_fixed_points():
+    for code, val in E4M3_FIXED_POINTS.items():
+        got = ref.e4m3_to_f64(np.array([code], dtype=np.uint8))[0]
+        assert got == val and math.copysign(1.0, got) == math.copysign(1.0, val), hex(code)
+
+
+def test_e4m3_nan_codes_and_ordering():
+    allv = ref.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    assert sorted(np.flatnonzero(np.isnan(allv)).tolist()) == [0x7F, 0xFF]
+    pos = allv[:0x7F]
+    assert np.all(np.diff(pos) > 0)                       # codes 0x00..0x7E increase strictly
+    assert np.array_equal(allv[0x80:0xFF], -pos)          # the sign bit only flips the sign
+    # every normal value has at most 4 significant bits, every subnormal is a multiple of 2^-9
+    normal = pos[8:]
+    m, _ = np.frexp(normal)
+    assert np.all((m * 16) == np.round(m * 16))
+    assert np.all((pos[:8] * 2 ** 9) == np.arange(8))
+
+
+# ------------------------------------------------------ the input quantiser
+
+def test_quantiser_round_trips_and_rounds_to_nearest_even():
+    grid = ref.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert np.array_equal(ref.e4m3_to_f64(inputs.e4m3_bits_from_f64(grid)), grid)
+    assert np.array_equal(ref.e4m3_to_f64(inputs.e4m3_bits_from_f64(-grid[1:])), -grid[1:])
+    # ties: 1.0625 lies halfway between 1 (even code 0x38) and 1.125 (odd 0x39)
+    cases = {1.0625: 1.0, 1.1875: 1.25, 2.0 ** -10: 0.0, 1.5 * 2.0 ** -9: 2.0 ** -8, 300.0: 288.0, 0.1: 0.1015625}
+    for x, want in cases.items():
+        assert ref.e4m3_to_f64(inputs.e4m3_bits_from_f64(np.array([x])))[0] == want, x
+    with pytest.raises(ValueError):
+        inputs.e4m3_bits_from_f64(np.array([449.0]))
+
+
+def test_per_head_quantisation():
+    x = np.random.Generator(np.random.PCG64(3)).standard_normal((2, 3, 40, 16))
+    x[1, 2] *= 50.0
+    bits, s = inputs.quantize_e4m3_per_head(x)
+    assert s.dtype == np.float32 and s.shape == (2, 3)
+    vals = ref.e4m3_to_f64(bits) * s.astype(np.float64)[:, :, None, None]
+    for b in range(2):
+        for h in range(3):
+            # the largest magnitude of each head lands on 448 (up to the fp32 factor)
+            assert np.max(np.abs(ref.e4m3_to_f64(bits[b, h]))) == 448.0
+            err = np.abs(vals[b, h] - x[b, h])
+            assert np.all(err <= 2.0 ** -4 * np.abs(x[b, h]) + 2.0 ** -10 * s[b, h] * 1.0001)
+
+
+# ----------------------------------------------------- the fp8 forward oracle
+
+def _ones(shape):
+    return np.ones(shape, dtype=np.float32)
+
+
+def test_zero_queries_average_the_values_and_v_is_transposed():
+    B, Hq, Hkv, T, d = 1, 2, 1, 6, 4
+    q8 = np.zeros((B, Hq, T, d), dtype=np.uint8)
+    k8 = inputs.e4m3_bits_from_f64(np.random.Generator(np.random.PCG64(1)).uniform(-4, 4, (B, Hkv, T, d)))
+    vt8 = np.zeros((B, Hkv, d, T), dtype=np.uint8)
+    vt8[0, 0, 1, 4] = 0x48            # V[key 4, dim 1] = 4.0, stored at V^T[dim 1, key 4]
+    vs = np.array([[0.5]], dtype=np.float32)
+    o, lse = ref.attention_fwd_fp8(q8, k8, vt8, _ones((B, Hq)), _ones((B, Hkv)), vs, 0.3, False)
+    want = np.zeros((B, Hq, T, d))
+    want[..., 1] = 4.0 * 0.5 / T      # zero scores: O is the mean of the values
+    assert np.allclose(o, want, rtol=1e-15, atol=0)
+    assert np.allclose(lse, math.log(T), rtol=1e-15)
+    # causal: row i averages keys 0..i, so only rows i >= 4 see key 4
+    o, lse = ref.attention_fwd_fp8(q8, k8, vt8, _ones((B, Hq)), _ones((B, Hkv)), vs, 0.3, True)
+    for i in range(T):
+        assert o[0, 0, i, 1] == (2.0 / (i + 1) if i >= 4 else 0.0)
+        assert np.all(o[0, 0, i, [0, 2, 3]] == 0.0)
+        assert math.isclose(lse[0, 0, i], math.log(i + 1), rel_tol=1e-15, abs_tol=1e-15)
+
+
+def test_two_keys_closed_form_with_factors():
+    # one query per head, two keys per kv head, d = 1, one kv head per query head:
+    # O = (v0 e^{s0} + v1 e^{s1}) / (e^{s0} + e^{s1}) with every factor applied
+    q8 = np.array([[[[0x40]], [[0x38]]]], dtype=np.uint8)                     # 2.0 | 1.0
+    k8 = np.array([[[[0x38], [0xC2]], [[0x30], [0x48]]]], dtype=np.uint8)     # 1.0, -2.5 | 0.5, 4.0
+    vt8 = np.array([[[[0x48, 0x30]], [[0x4F, 0xB8]]]], dtype=np.uint8)        # V = 4.0, 0.5 | 7.5, -1.0
+    qs = np.array([[0.25, 0.5]], np.float32)
+    ks = np.array([[2.0, 0.125]], np.float32)
+    vs = np.array([[3.0, 1.5]], np.float32)
+    scale = 0.75
+    o, lse = ref.attention_fwd_fp8(q8, k8, vt8, qs, ks, vs, scale, False)
+    heads = [((2.0, 0.25), ((1.0, -2.5), 2.0), ((4.0, 0.5), 3.0)),
+             ((1.0, 0.5), ((0.5, 4.0), 0.125), ((7.5, -1.0), 1.5))]
+    for h, ((qv, qf), (kvs, kf), (vvs, vf)) in enumerate(heads):
+        s = [scale * (qv * qf) * (kx * kf) for kx in kvs]
+        vals = [vx * vf for vx in vvs]
+        want = (vals[0] * math.exp(s[0]) + vals[1] * math.exp(s[1])) / (math.exp(s[0]) + math.exp(s[1]))
+        assert math.isclose(o[0, h, 0, 0], want, rel_tol=1e-14), h
+        assert math.isclose(lse[0, h, 0], math.log(math.exp(s[0]) + math.exp(s[1])), rel_tol=1e-14), h
+
+
+def test_factors_stay_with_their_heads():
+    # GQA: 4 query heads on 2 kv heads; changing one head's factor changes that head only
+    d = inputs.draw_fp8_attention_inputs(7, 1, 4, 2, 9, 9, 8)
+    base = ref.attention_fwd_fp8(d["q8"], d["k8"], d["vt8"], d["q_scale"], d["k_scale"], d["v_scale"], 0.5, True)
+    qs = d["q_scale"].copy()
+    qs[0, 1] *= 2
+    o, l = ref.attention_fwd_fp8(d["q8"], d["k8"], d["vt8"], qs, d["k_scale"], d["v_scale"], 0.5, True)
+    changed = [not np.array_equal(o[0, h], base[0][0, h]) for h in range(4)]
+    assert changed == [False, True, False, False]
+    vs = d["v_scale"].copy()
+    vs[0, 1] *= 3                     # kv head 1 serves query heads 2 and 3; O is linear in V
+    o, l = ref.attention_fwd_fp8(d["q8"], d["k8"], d["vt8"], d["q_scale"], d["k_scale"], vs, 0.5, True)
+    assert np.array_equal(o[0, :2], base[0][0, :2])
+    assert np.allclose(o[0, 2:], 3 * base[0][0, 2:], rtol=1e-14, atol=0)
+    assert np.array_equal(l, base[1])
+
+
+def test_draw_recipe_shapes_and_determinism():
+    a = inputs.draw_fp8_attention_inputs(3, 1, 4, 2, 33, 48, 64)
+    b = inputs.draw_fp8_attention_inputs(3, 1, 4, 2, 33, 48, 64)
+    assert a["q8"].shape == (1, 4, 33, 64) and a["k8"].shape == (1, 2, 48, 64) and a["vt8"].shape == (1, 2, 64, 48)
+    assert a["q_scale"].shape == (1, 4) and a["k_scale"].shape == (1, 2) and a["v_scale"].shape == (1, 2)
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+    assert not np.isnan(ref.e4m3_to_f64(a["q8"])).any()

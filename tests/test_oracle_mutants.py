@@ -122,3 +122,34 @@ def test_window_mutant_is_caught(name, monkeypatch):
             failed = True
             break
     assert failed, name
+
+
+FP8_MUTANTS = {
+    "exponent bias 8": ("np.exp2((e - 7).astype(np.float64))", "np.exp2((e - 8).astype(np.float64))"),
+    "subnormals as normals": ("np.where(e == 0, (f / 8.0) * 2.0 ** -6,", "np.where(e < 0, (f / 8.0) * 2.0 ** -6,"),
+    "subnormal step 2^-7": ("(f / 8.0) * 2.0 ** -6", "(f / 8.0) * 2.0 ** -7"),
+    "S.1111.111 not NaN": ("mag = np.where((e == 15) & (f == 7), np.nan, mag)", "pass"),
+    "V not transposed back": ("v = np.swapaxes(e4m3_to_f64(vt8), 2, 3)", "v = e4m3_to_f64(vt8).reshape(np.swapaxes(vt8, 2, 3).shape)"),
+    "q factor ignored": ("q = e4m3_to_f64(q8) * np.asarray(q_scale", "q = e4m3_to_f64(q8) * 0 + e4m3_to_f64(q8) * np.ones_like(q_scale"),
+    "v factor ignored": ("np.swapaxes(e4m3_to_f64(vt8), 2, 3) * np.asarray(v_scale", "np.swapaxes(e4m3_to_f64(vt8), 2, 3) * np.ones_like(v_scale"),
+    "k factor from the query heads": ("k = e4m3_to_f64(k8) * np.asarray(k_scale, dtype=np.float64)[:, :, None, None]",
+                                       "k = e4m3_to_f64(k8) * np.asarray(k_scale, dtype=np.float64)[:, ::-1, None, None]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    from tests import test_oracle_fp8 as tf
+    mod = _mutant(*FP8_MUTANTS[name])
+    monkeypatch.setattr(tf, "ref", mod)
+    checks = [tf.test_e4m3_fixed_points, tf.test_e4m3_nan_codes_and_ordering,
+              tf.test_zero_queries_average_the_values_and_v_is_transposed,
+              tf.test_two_keys_closed_form_with_factors, tf.test_factors_stay_with_their_heads]
+    failed = False
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failed = True
+            break
+    assert failed, name
