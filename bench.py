@@ -53,6 +53,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (AMD spec)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak (AMD spec)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak (AMD spec)
 
 COPY_BYTES = 1 << 30          # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -80,6 +81,7 @@ TRAFFIC_UNITS = {
     "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false>", "bwd_dkdv_kernel<128, true, false>"],
     "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true>"],
     "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["bwd_dq_kernel<128, true, true>", "bwd_dkdv_kernel<128, true, true>"],
+    "fa_fwd_fp8 causal B1 H32 T8192 d128": ["fwd_fp8_kernel<128, true>"],
 }
 
 
@@ -272,6 +274,41 @@ def run_window(steps, warmup):
     return {"fwd_ms": t_f.median_ms(), "bwd_ms": t_b.median_ms(), "fwd_flop": ff, "bwd_flop": 2.5 * ff}
 
 
+def run_fp8(steps, warmup):
+    """fp8 forward on the causal long-context shape (B1 H32 T8192 d128): Q, K, V
+    drawn N(0,1), quantised per (batch, head) to e4m3 (largest magnitude on 448),
+    V handed over transposed."""
+    import torch
+    from io_aware_softmax_05_amd import fa
+    B, H, T, d = 1, 32, 8192, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+
+    def quant(x):
+        s = (x.abs().amax(dim=(2, 3)) / 448.0).clamp_min(1e-30)
+        return (x / s[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8), s.float().contiguous()
+
+    q8, qs = quant(torch.randn((B, H, T, d), generator=gen, device="cuda"))
+    k8, ks = quant(torch.randn((B, H, T, d), generator=gen, device="cuda"))
+    v8, vs = quant(torch.randn((B, H, T, d), generator=gen, device="cuda"))
+    vt8 = v8.transpose(2, 3).contiguous()
+    o = torch.empty((B, H, T, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    t = Timer(stream)
+
+    def call():
+        fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o, lse, B, H, H, T, T, d, d ** -0.5, True, stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        t.record(call)
+    torch.cuda.synchronize()
+    return {"median_ms": t.median_ms(), "flop": fwd_flops(B, H, T, T, d, True)}
+
+
 def run_small_f32(steps, warmup):
     """The single-head fp32 workload (B1 H1 T256 d64): latency only."""
     import torch
@@ -296,11 +333,12 @@ def run_small_f32(steps, warmup):
     return {"median_ms": t.median_ms(), "flop": fwd_flops(1, 1, 256, 256, 64, False)}
 
 
-def roofline(bound, work, ms, unit_name, algorithmic_bytes=None):
-    """Roofline entry for one launch unit: `work` is FLOP (bound "mfma") or
-    bytes (bound "hbm") per launch, `ms` the mean launch duration."""
+def roofline(bound, work, ms, unit_name, algorithmic_bytes=None, peak_tflops=PEAK_BF16_TFLOPS):
+    """Roofline entry for one launch unit: `work` is FLOP (bound "mfma", against
+    the matrix peak of the unit's dtype) or bytes (bound "hbm") per launch, `ms`
+    the mean launch duration."""
     if bound == "mfma":
-        achieved, peak, unit = work / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, peak_tflops, "TFLOP/s"
     else:
         achieved, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     out = {"kernel": unit_name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -446,7 +484,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the causal 8k and decode measurements")
-    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "decode", "copy"],
+    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "causal-8k-fp8", "decode", "copy"],
                     help="run one measurement alone (profiling runs); 'copy' runs a plain device copy "
                          "of 1 GiB, the calibration for HBM byte counters")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -470,6 +508,9 @@ def main():
         r = run_attention("causal-8k-fwd", args.steps, args.warmup, backward=False)
         r.pop("host")
         print(json.dumps(r), flush=True)
+        return 0
+    if args.only == "causal-8k-fp8":
+        print(json.dumps(run_fp8(args.steps, args.warmup)), flush=True)
         return 0
     if args.only == "decode":
         print(json.dumps(run_decode(args.steps, args.warmup)), flush=True)
@@ -528,6 +569,10 @@ def main():
             "mfma", sw["fwd_flop"], sw["fwd_ms"], "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128")
         out["targets"]["fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128"] = roofline(
             "mfma", sw["bwd_flop"], sw["bwd_ms"], "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128")
+        torch.cuda.empty_cache()
+        f8 = run_fp8(50, 10)
+        out["targets"]["fa_fwd_fp8 causal B1 H32 T8192 d128"] = roofline(
+            "mfma", f8["flop"], f8["median_ms"], "fa_fwd_fp8 causal B1 H32 T8192 d128", peak_tflops=PEAK_FP8_TFLOPS)
         f32 = run_small_f32(50, 10)
         out["latency"] = {"fa_fwd_f32 B1 H1 T256 d64": {"median_us": round(f32["median_ms"] * 1e3, 2),
                                                         "flop": f32["flop"], "bound": "latency"}}
