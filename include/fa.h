@@ -115,7 +115,7 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
  *   o [B,Hq,Tq,d] bf16 and lse [B,Hq,Tq] fp32 (written; lse may be NULL)
  * Computes softmax(scale * Q K^T (+ causal mask)) V on the dequantised values.
  * QK^T and PV run on fp8 matrix cores with fp32 accumulation; the
- * probabilities (times 2^6, at most 2^8) are rounded to e4m3 before the PV
+ * probabilities (times 2^5, at most 2^8) are rounded to e4m3 before the PV
  * product, the running sum uses them unrounded, so O carries a relative error
  * of up to 2^-4 per probability, LSE only the score rounding.
  * Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for NULL vt/q_scale/k_scale/

@@ -14,11 +14,11 @@
 //     writes that layout at no extra cost).
 //   * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales;
 //     scale * log2(e) * q_scale * k_scale folds into the exponent's FMA.
-//   * P' = 2^(S c - m + 6) is rounded to e4m3 for O^T += V^T P'^T. The running
-//     maximum m moves only when a row grows by more than 2^2, so P' <= 2^8,
-//     inside e4m3's range (448); the shift keeps probabilities down to 2^-12
+//   * P' = 2^(S c - m + 5) is rounded to e4m3 for O^T += V^T P'^T. The running
+//     maximum m moves only when a row grows by more than 2^3, so P' <= 2^8,
+//     inside e4m3's range (448); the shift keeps probabilities down to 2^-11
 //     of the reference in e4m3's normal range. The row sum l uses the
-//     unrounded fp32 P', and O = v_scale * O' / l (the 2^6 cancels).
+//     unrounded fp32 P', and O = v_scale * O' / l (the 2^5 cancels).
 //
 // gfx950 mapping (rows and tiles as in the bf16 forward: 32 queries per wave,
 // 64-key tiles, two-stage software pipeline, one barrier per tile)
@@ -69,8 +69,8 @@ __device__ __forceinline__ uint32_t swk(uint32_t r) {
 }
 __device__ __forceinline__ uint32_t swv(uint32_t r) { return (r >> 2) & 3u; }
 
-constexpr float kSlack8 = 2.f;   // the reference maximum moves when a row grows by more than 2^2
-constexpr float kShift8 = 6.f;   // P' = 2^(S c - m + 6) <= 2^8
+constexpr float kSlack8 = 3.f;   // the reference maximum moves when a row grows by more than 2^3
+constexpr float kShift8 = 5.f;   // P' = 2^(S c - m + 5) <= 2^8
 
 }  // namespace
 
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
         pw[4 * kb + r / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
       }
     const i32x8 pb = i32x8{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-    __builtin_amdgcn_iglp_opt(2);
+    __builtin_amdgcn_iglp_opt(0);
     // stage B: O'^T[d, query] += V^T[d, key] P'^T[key, query]
     pv(j & 1, pb);
     l += lsum;
