@@ -7,5 +7,6 @@ tables), and imports nothing from it.
 
   attention_ref  -- three-step S -> P -> O forward, backward, decode
   online_model   -- the per-row online-softmax recurrence and partial merge
+  philox         -- Philox counter-based random numbers (the dropout mask)
 """
-from . import attention_ref, online_model  # noqa: F401
+from . import attention_ref, online_model, philox  # noqa: F401

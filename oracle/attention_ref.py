@@ -35,7 +35,12 @@ Readings taken where the pages are silent (each is pinned by a test):
     definition) of W >= 1 keys is read as a causal band: key j is visible to query
     i iff i + (Tk - Tq) - W < j <= i + (Tk - Tq), i.e. each query sees its
     own position and the W - 1 keys before it; in decoding the one query
-    sees the last W cached keys. W = 0 means no window.
+    sees the last W cached keys. W = 0 means no window;
+  * dropout (zerotofrontier page, section "Real code moves even more": a
+    training forward pass applies it to the probabilities before the final
+    product) keeps P_ij with probability kappa = t / 256 and scales kept
+    entries by 1 / kappa, so O = (P * Z / kappa) V with the keep mask Z of
+    `dropout_keep`; the log-sum-exp is that of the softmax before dropout.
 
 Rows are independent, so every function may work on any subset of query rows
 (the full-size checks evaluate sampled rows one block at a time). Keys are
@@ -43,9 +48,64 @@ never split: each row always sees its whole score row at once.
 """
 from __future__ import annotations
 
+from dataclasses import dataclass
+
 import numpy as np
 
+from .philox import philox4x32_10
+
 _ROW_BLOCK = 512
+
+
+@dataclass(frozen=True)
+class Dropout:
+    """Dropout of the attention probabilities.
+
+    t in [1, 256] is the keep threshold (keep probability kappa = t / 256);
+    seed (64 bits) and offset (32 bits) choose the random stream."""
+    t: int
+    seed: int
+    offset: int = 0
+
+    @property
+    def kappa(self) -> float:
+        return self.t / 256.0
+
+
+def keep_threshold(p_drop: float) -> int:
+    """Keep threshold for a dropout probability: t = (1 - p) * 256 rounded to
+    the nearest integer (ties to even), valid when 1 <= t <= 256."""
+    t = round((1.0 - float(p_drop)) * 256.0)
+    if not (0.0 <= float(p_drop) < 1.0) or not 1 <= t <= 256:
+        raise ValueError(f"dropout probability {p_drop} gives no usable keep threshold")
+    return int(t)
+
+
+def dropout_keep(drop: Dropout, bh: int, rows, Tk: int) -> np.ndarray:
+    """Boolean [len(rows), Tk]: is P[i, j] of flattened head bh = b * Hq + h kept?
+
+    Random-number contract: for query row i and the 16 keys 16 g .. 16 g + 15,
+    one Philox-4x32-10 call with counter (g, i, bh, offset) and key
+    (seed mod 2^32, seed div 2^32) gives four words; key j uses byte j mod 16
+    of them, byte n being bits 8 (n mod 4) .. 8 (n mod 4) + 7 of word n div 4.
+    The entry is kept iff that byte is below t."""
+    rows = np.asarray(rows, dtype=np.int64)
+    n_groups = (Tk + 15) // 16
+    g = np.arange(n_groups, dtype=np.int64)
+    words = philox4x32_10(g[None, :], rows[:, None], bh, drop.offset,
+                          drop.seed & 0xFFFFFFFF, (drop.seed >> 32) & 0xFFFFFFFF)
+    w = np.stack(words, axis=-1).astype(np.uint32)            # [n, groups, word]
+    b = w[..., None] >> (np.arange(4, dtype=np.uint32) * 8)   # [n, groups, word, byte]
+    bytes_ = (b & 0xFF).reshape(rows.shape[0], n_groups * 16)[:, :Tk]
+    return bytes_ < drop.t
+
+
+def _dropped(p: np.ndarray, drop, bh: int, rows, Tk: int):
+    """(P * Z / kappa, Z / kappa) for the rows of one head; (P, 1) without dropout."""
+    if drop is None:
+        return p, 1.0
+    z = dropout_keep(drop, bh, rows, Tk) / drop.kappa
+    return p * z, z
 
 
 def visible(rows: np.ndarray, Tq: int, Tk: int, causal: bool, window: int = 0) -> np.ndarray:
@@ -87,10 +147,11 @@ def _kv_head(hq: int, Hq: int, Hkv: int) -> int:
     return hq // (Hq // Hkv)
 
 
-def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, window: int = 0):
+def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, window: int = 0, dropout=None):
     """Forward: O [B,Hq,n,d] and LSE [B,Hq,n] for query rows `rows` (all if None).
 
-    q [B,Hq,Tq,d]; k, v [B,Hkv,Tk,d]; any float dtype, computed in fp64."""
+    q [B,Hq,Tq,d]; k, v [B,Hkv,Tk,d]; any float dtype, computed in fp64.
+    `dropout` (a Dropout or None) drops probabilities before the product with V."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -106,7 +167,8 @@ def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, window: int = 
             for s in range(0, rows.shape[0], _ROW_BLOCK):
                 r = rows[s:s + _ROW_BLOCK]
                 p, l = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal, window)
-                o[b, h, s:s + _ROW_BLOCK] = p @ v[b, hk]
+                pd, _ = _dropped(p, dropout, b * Hq + h, r, k.shape[2])
+                o[b, h, s:s + _ROW_BLOCK] = pd @ v[b, hk]
                 lse[b, h, s:s + _ROW_BLOCK] = l
     return o, lse
 
@@ -143,11 +205,13 @@ def attention_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, scale: float, caus
     return attention_fwd(q, k, v, scale, causal, rows)
 
 
-def attention_bwd(q, k, v, do, scale: float, causal: bool, window: int = 0):
+def attention_bwd(q, k, v, do, scale: float, causal: bool, window: int = 0, dropout=None):
     """Backward of O = softmax(scale Q K^T [+mask]) V given dO.
 
     Returns dQ [B,Hq,Tq,d], dK and dV [B,Hkv,Tk,d] in fp64. P is recomputed
-    here from Q and K (this oracle never sees the GPU's O or LSE)."""
+    here from Q and K (this oracle never sees the GPU's O or LSE). With
+    dropout, O = Pd V with Pd = P Z / kappa, so dV = Pd^T dO and the softmax
+    sees dP = (dO V^T) Z / kappa."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -163,16 +227,18 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool, window: int = 0):
             for s in range(0, Tq, _ROW_BLOCK):
                 r = np.arange(s, min(Tq, s + _ROW_BLOCK))
                 p, _ = row_probs(q[b, h, r], k[b, hk], scale, r, Tq, causal, window)
+                pd, z = _dropped(p, dropout, b * Hq + h, r, k.shape[2])
                 g = do[b, h, r]
-                dv[b, hk] += p.T @ g
-                dp = g @ v[b, hk].T
+                dv[b, hk] += pd.T @ g
+                dp = (g @ v[b, hk].T) * z
                 ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
                 dq[b, h, r] = scale * (ds @ k[b, hk])
                 dk[b, hk] += scale * (ds.T @ q[b, h, r])
     return dq, dk, dv
 
 
-def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows, window: int = 0):
+def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows, window: int = 0,
+                          dropout=None):
     """dQ for some query rows of one (batch, query head): each row's gradient
     needs only that row's own scores, so it can be evaluated at any size."""
     q = np.asarray(q[b, h], dtype=np.float64)
@@ -183,13 +249,15 @@ def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: in
     rows = np.asarray(rows, dtype=np.int64)
     Tq = q.shape[0]
     p, _ = row_probs(q[rows], kk, scale, rows, Tq, causal, window)
+    _, z = _dropped(p, dropout, b * Hq + h, rows, kk.shape[0])
     g = np.asarray(do[b, h], dtype=np.float64)[rows]
-    dp = g @ vv.T
+    dp = (g @ vv.T) * z
     ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     return scale * (ds @ kk)
 
 
-def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk: int, keys, window: int = 0):
+def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk: int, keys, window: int = 0,
+                            dropout=None):
     """dK and dV for some keys of one (batch, KV head).
 
     A key's gradient sums contributions of every query row of the group that
@@ -216,9 +284,10 @@ def attention_bwd_dkdv_keys(q, k, v, do, scale: float, causal: bool, b: int, hk:
         for s in range(first, stop, _ROW_BLOCK):
             r = np.arange(s, min(stop, s + _ROW_BLOCK))
             p, _ = row_probs(qq[r], kk, scale, r, Tq, causal, window)
-            dp = gg[r] @ vv.T
+            pd, z = _dropped(p, dropout, b * Hq + h, r, Tk)
+            dp = (gg[r] @ vv.T) * z
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-            dv += p[:, keys].T @ gg[r]
+            dv += pd[:, keys].T @ gg[r]
             dk += scale * (ds[:, keys].T @ qq[r])
     return dk, dv
 
