@@ -5,6 +5,7 @@ Each mutant is the oracle's own source with one textual edit, executed as a
 separate module; the real oracle is never modified.
 """
 import inspect
+import sys
 import types
 
 import numpy as np
@@ -17,8 +18,14 @@ from tests import oracle_pins as pins
 def _mutant(old: str, new: str) -> types.ModuleType:
     src = inspect.getsource(ref)
     assert old in src, old
-    mod = types.ModuleType("oracle_mutant")
-    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    name = "oracle._mutant"
+    mod = types.ModuleType(name)
+    mod.__package__ = "oracle"   # the oracle imports its Philox module relatively
+    sys.modules[name] = mod      # dataclasses look their module up by name
+    try:
+        exec(compile(src.replace(old, new, 1), name, "exec"), mod.__dict__)
+    finally:
+        del sys.modules[name]
     return mod
 
 
@@ -39,7 +46,7 @@ FWD_MUTANTS = {
     "max missing from lse": ("lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))", "lse = np.where(empty, -np.inf, np.log(l_safe))"),
     "not normalised": ("p = e / l_safe[:, None]", "p = e"),
     "wrong kv head map": ("return hq // (Hq // Hkv)", "return hq % Hkv"),
-    "values swapped for keys": ("o[b, h, s:s + _ROW_BLOCK] = p @ v[b, hk]", "o[b, h, s:s + _ROW_BLOCK] = p @ k[b, hk]"),
+    "values swapped for keys": ("o[b, h, s:s + _ROW_BLOCK] = pd @ v[b, hk]", "o[b, h, s:s + _ROW_BLOCK] = pd @ k[b, hk]"),
 }
 
 
@@ -82,8 +89,8 @@ BWD_MUTANTS = {
     "row term sign": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * (dp + (p * dp).sum(axis=1, keepdims=True))"),
     "dq scale dropped": ("dq[b, h, r] = scale * (ds @ k[b, hk])", "dq[b, h, r] = ds @ k[b, hk]"),
     "dk uses dO": ("dk[b, hk] += scale * (ds.T @ q[b, h, r])", "dk[b, hk] += scale * (ds.T @ g)"),
-    "dv overwritten per group": ("dv[b, hk] += p.T @ g", "dv[b, hk] = p.T @ g"),
-    "dp not transposed": ("dp = g @ v[b, hk].T", "dp = g @ v[b, hk][::-1].T"),
+    "dv overwritten per group": ("dv[b, hk] += pd.T @ g", "dv[b, hk] = pd.T @ g"),
+    "dp not transposed": ("dp = (g @ v[b, hk].T) * z", "dp = (g @ v[b, hk][::-1].T) * z"),
 }
 
 
