@@ -72,16 +72,21 @@ DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
 # Launch units whose HBM traffic is recorded: unit -> kernel names (prefix of
 # the demangled name, up to the argument list).
 TRAFFIC_UNITS = {
-    "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false, false>"],
-    "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false, false>", "bwd_dkdv_kernel<64, false, false>"],
+    "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false, false, false>"],
+    "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false, false, false>", "bwd_dkdv_kernel<64, false, false, false>"],
     # the causal 8k and 32k forwards run the same kernel: told apart by grid size (threads)
-    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true, false>@524288"],
+    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true, false, false>@524288"],
     "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128, 3>", "decode_merge_kernel<128>"],
-    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false>@2097152"],
-    "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false>", "bwd_dkdv_kernel<128, true, false>"],
-    "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true>"],
-    "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["bwd_dq_kernel<128, true, true>", "bwd_dkdv_kernel<128, true, true>"],
+    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false, false>@2097152"],
+    "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false, false>",
+                                                   "bwd_dkdv_kernel<128, true, false, false>"],
+    "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true, false>"],
+    "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["bwd_dq_kernel<128, true, true, false>",
+                                                     "bwd_dkdv_kernel<128, true, true, false>"],
     "fa_fwd_fp8 causal B1 H32 T8192 d128": ["fwd_fp8_kernel<128, true>"],
+    "fa_fwd_dropout B64 H16 T1024 d64 p0.1": ["fwd_bf16_kernel<64, false, false, true>"],
+    "fa_bwd_dropout B64 H16 T1024 d64 p0.1": ["bwd_dq_kernel<64, false, false, true>",
+                                              "bwd_dkdv_kernel<64, false, false, true>"],
 }
 
 
@@ -143,7 +148,11 @@ class Timer:
         return float(np.median([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
 
-def run_attention(name, steps, warmup, backward=True):
+DROPOUT_P = 0.1                # attention dropout of the GPT-2-medium layer with dropout
+DROPOUT_SEED, DROPOUT_OFFSET = 0x5EED, 0
+
+
+def run_attention(name, steps, warmup, backward=True, p_drop=0.0):
     import torch
     from io_aware_softmax_05_amd import fa
     B, Hq, Hkv, T, d, causal, seed = WORKLOADS[name]
@@ -163,10 +172,18 @@ def run_attention(name, steps, warmup, backward=True):
     t_fwd, t_bwd = Timer(stream), Timer(stream)
 
     def f():
-        fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, stream)
+        if p_drop > 0:
+            fa.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, p_drop, DROPOUT_SEED,
+                              DROPOUT_OFFSET, stream)
+        else:
+            fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, stream)
 
     def b():
-        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, scale, causal, stream)
+        if p_drop > 0:
+            fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, scale, causal,
+                              p_drop, DROPOUT_SEED, DROPOUT_OFFSET, stream)
+        else:
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, scale, causal, stream)
 
     for _ in range(warmup):
         f()
@@ -484,7 +501,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the causal 8k and decode measurements")
-    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "causal-8k-fp8", "decode", "copy"],
+    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "causal-8k-fp8", "decode", "dropout", "copy"],
                     help="run one measurement alone (profiling runs); 'copy' runs a plain device copy "
                          "of 1 GiB, the calibration for HBM byte counters")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -514,6 +531,11 @@ def main():
         return 0
     if args.only == "decode":
         print(json.dumps(run_decode(args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "dropout":
+        r = run_attention("gpt2-medium-fwd-bwd", args.steps, args.warmup, backward=True, p_drop=DROPOUT_P)
+        r.pop("host")
+        print(json.dumps(r), flush=True)
         return 0
     if args.only == "copy":
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -573,6 +595,14 @@ def main():
         f8 = run_fp8(50, 10)
         out["targets"]["fa_fwd_fp8 causal B1 H32 T8192 d128"] = roofline(
             "mfma", f8["flop"], f8["median_ms"], "fa_fwd_fp8 causal B1 H32 T8192 d128", peak_tflops=PEAK_FP8_TFLOPS)
+        torch.cuda.empty_cache()
+        dr = run_attention("gpt2-medium-fwd-bwd", 20, 5, backward=True, p_drop=DROPOUT_P)
+        dr.pop("host")
+        out["targets"]["fa_fwd_dropout B64 H16 T1024 d64 p0.1"] = roofline(
+            "mfma", dr["fwd_flop"], dr["fwd_median_ms"], "fa_fwd_dropout B64 H16 T1024 d64 p0.1")
+        out["targets"]["fa_bwd_dropout B64 H16 T1024 d64 p0.1"] = roofline(
+            "mfma", dr["bwd_flop"], dr["bwd_median_ms"], "fa_bwd_dropout B64 H16 T1024 d64 p0.1",
+            bwd_algorithmic_bytes(B, Hq, Hkv, T, d))
         f32 = run_small_f32(50, 10)
         out["latency"] = {"fa_fwd_f32 B1 H1 T256 d64": {"median_us": round(f32["median_ms"] * 1e3, 2),
                                                         "flop": f32["flop"], "bound": "latency"}}

@@ -44,6 +44,7 @@
 #define FA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -169,6 +170,55 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int window,
                   hipStream_t stream);
+
+/*
+ * Dropout of the attention probabilities in the fused forward and backward.
+ * The zerotofrontier page "Efficient attention: memory-bound" (section "Real
+ * code moves even more") lists dropout among the elementwise steps a training
+ * forward pass applies to the probabilities before the product with V; the
+ * pages give no random-number contract. The one fixed here:
+ *   - keep threshold t = round((1 - p_drop) * 256) (ties to even), which must
+ *     lie in [1, 256]; an entry is kept with probability t / 256 and kept
+ *     entries are scaled by 256 / t, so O = (P * Z) V * 256 / t;
+ *   - for query row i of flattened head bh = b * Hq + h and the 16 keys
+ *     16 g .. 16 g + 15, one Philox-4x32-10 call (Salmon, Moraes, Dror and
+ *     Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) with counter
+ *     (g, i, bh, offset) and key (seed mod 2^32, seed >> 32) yields four
+ *     32-bit words; key j takes byte j mod 16 (byte n = bits 8 (n mod 4) ..
+ *     8 (n mod 4) + 7 of word n / 4) and is kept iff that byte is below t;
+ *   - the log-sum-exp is that of the softmax before dropout, so the forward's
+ *     lse feeds fa_bwd_dropout unchanged.
+ * The same (p_drop, seed, offset) must be passed to the forward and the
+ * backward of one layer; distinct offsets (or seeds) give independent masks.
+ */
+
+/* Keep threshold t in [1, 256] for a dropout probability p_drop in [0, 1), or
+ * FA_ERR_INVALID_ARG when p_drop is not finite, outside [0, 1), or so close
+ * to 1 that t would be 0. */
+int fa_dropout_keep_threshold(float p_drop);
+
+/*
+ * Forward with dropout: the parameters of fa_fwd plus p_drop, seed and
+ * offset (see above); d, layout, ownership and errors as fa_fwd, plus
+ * FA_ERR_INVALID_ARG for an unusable p_drop. p_drop = 0 (t = 256) keeps
+ * every entry and runs the plain forward.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+                   float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream);
+
+/*
+ * Backward of fa_fwd_dropout with the same (p_drop, seed, offset): the mask
+ * is regenerated, never stored. o and lse are the dropout forward's outputs.
+ * dV = (P * Z)^T dO * 256 / t, the softmax gradient takes
+ * dP = (dO V^T) * Z * 256 / t, and rowsum(dO * O) still equals
+ * sum_j P_ij dP_ij. Parameters, workspace and errors as fa_bwd, plus
+ * FA_ERR_INVALID_ARG for an unusable p_drop.
+ */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                   int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+                   float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream);
 
 /*
  * Workspace bytes fa_decode_splitkv needs for KV caches of up to Tk_max

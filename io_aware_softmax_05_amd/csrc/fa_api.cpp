@@ -30,6 +30,21 @@ int to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Dropout arguments for a usable p_drop (t in [1, 255]); t = 256 keeps
+// everything and is returned as "no dropout" (t = 0).
+int make_drop(float p_drop, uint64_t seed, uint32_t offset, fa::DropArgs* out) {
+  const int t = fa_dropout_keep_threshold(p_drop);
+  if (t < 0) return t;
+  *out = fa::DropArgs{};
+  if (t == 256) return FA_OK;
+  out->t = (uint32_t)t;
+  out->seed_lo = (uint32_t)seed;
+  out->seed_hi = (uint32_t)(seed >> 32);
+  out->offset = offset;
+  out->inv_keep = 256.f / (float)t;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -45,9 +60,16 @@ const char* fa_status_string(int status) {
   }
 }
 
+int fa_dropout_keep_threshold(float p_drop) {
+  if (!isfinite(p_drop) || p_drop < 0.f || p_drop >= 1.f) return FA_ERR_INVALID_ARG;
+  const double t = nearbyint((1.0 - (double)p_drop) * 256.0);   // default rounding: ties to even
+  if (t < 1.0 || t > 256.0) return FA_ERR_INVALID_ARG;
+  return (int)t;
+}
+
 static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int window,
-                    hipStream_t stream) {
+                    hipStream_t stream, const fa::DropArgs& drop = fa::DropArgs{}) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
   if (st != FA_OK) return st;
@@ -64,7 +86,17 @@ static int fwd_impl(const void* q, const void* k, const void* v, void* o, float*
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.c = scale * fa::kLog2eHost;
   a.window = window;
+  a.drop = drop;
   return to_status(fa::launch_fwd_bf16(a, d, causal != 0, stream));
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+                   float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream) {
+  fa::DropArgs drop;
+  const int st = make_drop(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, 0, stream, drop);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -137,7 +169,7 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d) {
 static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                     int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int window,
-                    hipStream_t stream) {
+                    hipStream_t stream, const fa::DropArgs& drop = fa::DropArgs{}) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
   if (st != FA_OK) return st;
@@ -164,7 +196,19 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   a.scale = scale;
   a.c = scale * fa::kLog2eHost;
   a.window = window;
+  a.drop = drop;
   return to_status(fa::launch_bwd(a, d, causal != 0, stream));
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                   int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
+                   float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream) {
+  fa::DropArgs drop;
+  const int st = make_drop(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale,
+                  causal, 0, stream, drop);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

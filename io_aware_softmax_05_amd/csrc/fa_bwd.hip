@@ -9,6 +9,11 @@
 // from dS, with the softmax Jacobian dS_ij = P_ij (dP_ij - D_i) and
 // D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic.
 //
+// With dropout (the DROP instantiations) both kernels regenerate the
+// forward's keep mask from the same Philox contract: dV = (P Z)^T dO / kappa,
+// dP is replaced by (dO V^T) Z / kappa, and D_i = rowsum(dO * O) still equals
+// sum_j P_ij dP_ij because O already carries the dropout.
+//
 // Two kernels, no atomics (the result is deterministic), dq first:
 //   dq    one workgroup per 32 query rows per wave (8 waves at d = 64, 4 at
 //         d = 128), laid out like the forward
@@ -71,11 +76,14 @@ struct DkdvCfg {
 // LDS through direct-to-LDS loads into a ring of C::NSTAGE tiles (the next
 // tile loads while one is consumed; at d = 64 two stages measured fastest);
 // tiles are stored unpadded with an XOR swizzle.
-template <int D, bool CAUSAL, class C = DkdvCfg<D>, bool WIN = false>
+template <int D, bool CAUSAL, class C = DkdvCfg<D>, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
   static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
+  static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
   constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
+  // dropout: a wave-private 32 x 32 byte tile turns row-major Philox bytes into key columns
+  constexpr int ZTILE = 32 * 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE + (DROP ? C::NW * ZTILE : 0)];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -181,10 +189,13 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
   const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
 
-  auto body = [&](const FA_LDS uint8_t* st, int q0, auto masked) {
+  FA_LDS uint8_t* ztile = smem + C::NSTAGE * STAGE + wave * ZTILE;
+
+  auto body = [&](const FA_LDS uint8_t* st, int q0, int head, auto masked) {
     const FA_LDS uint8_t* qt = st;
     const FA_LDS uint8_t* gt = st + QTILE;
     const FA_LDS uint8_t* stt = st + 2 * QTILE;
+    const uint32_t bhq = (uint32_t)(b * a.Hq + hk * G + head);   // flattened query head (dropout stream)
     // S = Q K^T and dP = dO V^T for BQ queries x 32 keys (one key per lane).
     f32x16 s[QB], dp[QB];
 #pragma unroll
@@ -203,7 +214,19 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     const int dbase = q0 + 4 * half + shift - key;
     uint32_t pw[QB][8], dsw[QB][8];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      // Dropout bytes for (row 32 qb + 8 g4 + 4 half + e, this lane's key), in
+      // register order 4 g4 + e. Lane (c, h) draws row 32 qb + c's bytes for
+      // the 16 keys kw0 + 16 h .. +15 (the forward's Philox contract), stores
+      // them row-major in the wave's tile and reads back its own key column.
+      uint32_t zbyte[16];
+      if constexpr (DROP) {
+        const u32x4 w = philox4x32_10((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
+                                      a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+        lds_write_b128(ztile, col * 32 + 16 * half, w);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zbyte[i] = ztile[(8 * (i >> 2) + 4 * half + (i & 3)) * 32 + col];
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int rq = qb * 32 + 8 * g4 + 4 * half;
@@ -220,14 +243,22 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
             const int dist = dbase + (qb * 32 + 8 * g4 + e);   // one unsigned compare for the band
             if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
           }
-          p[e] = pe;
-          ds[e] = pe * (dp[qb][r] - dl[e]);
+          float dpe = dp[qb][r];
+          float pv = pe;
+          if constexpr (DROP) {   // dV takes the kept P; dP is dropped and rescaled
+            const bool keep = zbyte[r] < a.drop.t;
+            pv = keep ? pe : 0.f;
+            dpe = keep ? dpe * a.drop.inv_keep : 0.f;
+          }
+          p[e] = pv;
+          ds[e] = pe * (dpe - dl[e]);
         }
         pw[qb][2 * g4] = pack_bf16x2(p[0], p[1]);
         pw[qb][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
         dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
         dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
       }
+    }
     // (the hint on the unmasked body only: on the masked one it costs registers)
     if constexpr (C::IGLP >= 0 && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(C::IGLP);
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
@@ -256,20 +287,23 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st);
     wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
   }
-  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = qt_begin;
+  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = qt_begin, cur_h = 0;
   for (int it = 0; it < n_iter; ++it) {
     issue(ld_stage);                      // tile it+NSTAGE-1 (zeros past the end)
     const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
     const int q0 = cur_qi * BQ;
     // some (row, key) pair of this wave is masked (causal limit or window start)
     if ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0))
-      body(st, q0, std::true_type{});
+      body(st, q0, cur_h, std::true_type{});
     else
-      body(st, q0, std::false_type{});
+      body(st, q0, cur_h, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();          // tile it+1 has landed; this stage is free
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
-    if (++cur_qi == n_qt) cur_qi = qt_begin;
+    if (++cur_qi == n_qt) {
+      cur_qi = qt_begin;
+      ++cur_h;
+    }
   }
   if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
@@ -285,8 +319,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
         const f32x16& vv = dv_acc[db];
         *(u32x2*)(dkp + d0) = u32x2{pack_bf16x2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale),
                                     pack_bf16x2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale)};
-        *(u32x2*)(dvp + d0) = u32x2{pack_bf16x2(vv[4 * g4], vv[4 * g4 + 1]),
-                                    pack_bf16x2(vv[4 * g4 + 2], vv[4 * g4 + 3])};
+        const float sv = DROP ? a.drop.inv_keep : 1.f;   // dV = (P Z)^T dO * 256 / t
+        *(u32x2*)(dvp + d0) = u32x2{pack_bf16x2(vv[4 * g4] * sv, vv[4 * g4 + 1] * sv),
+                                    pack_bf16x2(vv[4 * g4 + 2] * sv, vv[4 * g4 + 3] * sv)};
       }
   }
 }
@@ -329,9 +364,10 @@ struct DqCfg {
 // the last product from the accumulator registers. K and V arrive through
 // direct-to-LDS loads into a ring of C::NSTAGE tiles, swizzled like the
 // dK/dV kernel's tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
-template <int D, bool CAUSAL, class C = DqCfg<D>, bool WIN = false>
+template <int D, bool CAUSAL, class C = DqCfg<D>, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
+  static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
   constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
   constexpr int KB = BC / 32;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
@@ -454,7 +490,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     }
     uint32_t dsw[KB][8];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      u32x4 zb{};   // dropout bytes of this row's 32 keys (the forward's layout and contract)
+      if constexpr (DROP)
+        zb = dropout_bytes_32keys((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+                                  a.drop.seed_lo, a.drop.seed_hi, half);
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0 = exp2_fast(fmaf(s[kb][r], a.c, -lse2));
@@ -464,8 +504,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
           if (kr > lim || (WIN && kr < lo)) p0 = 0.f;
           if (kr + 1 > lim || (WIN && kr + 1 < lo)) p1 = 0.f;
         }
-        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp[kb][r] - delta), p1 * (dp[kb][r + 1] - delta));
+        float dp0 = dp[kb][r], dp1 = dp[kb][r + 1];
+        if constexpr (DROP) {   // dP of a dropped entry is 0, of a kept one scaled by 256 / t
+          dp0 = dropout_keep(zb, r, a.drop.t) ? dp0 * a.drop.inv_keep : 0.f;
+          dp1 = dropout_keep(zb, r + 1, a.drop.t) ? dp1 * a.drop.inv_keep : 0.f;
+        }
+        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp0 - delta), p1 * (dp1 - delta));
       }
+    }
     if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
     // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
 #pragma unroll
@@ -520,25 +566,32 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 
 // ---------------------------------------------------------------- launch
 
-template <int D, bool CAUSAL, bool WIN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DqCfg<D>, WIN>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DqCfg<D>, WIN, DROP>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
                      a, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // masked d = 64 tiles: 32-row query tiles (the 64-row masked body spills at
   // two waves per SIMD; measured 27% faster on a causal T2048 layer)
-  using KC = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>, DkdvCfg<D>>::type;
+  // causal d = 128 with dropout: 32-row tiles as well (the mask bytes push the
+  // 64-row masked body past 512 registers)
+  using KC = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
+             typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>, DkdvCfg<D>>::type>::type;
   const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0, stream,
                      a, n_ktiles);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream) {
   if (a.window > 0) return d == 64 ? launch<64, true, true>(a, stream) : launch<128, true, true>(a, stream);
+  if (a.drop.t != 0) {
+    if (d == 64) return causal ? launch<64, true, false, true>(a, stream) : launch<64, false, false, true>(a, stream);
+    return causal ? launch<128, true, false, true>(a, stream) : launch<128, false, false, true>(a, stream);
+  }
   if (d == 64) return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
   return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }

@@ -131,6 +131,55 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) {
   }
 }
 
+// Philox-4x32-10 counter-based generator (Salmon, Moraes, Dror and Shaw,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11, section 3.2 and
+// Table 2): ten rounds, each multiplying words 0 and 2 of the counter by the
+// two round multipliers, taking each 64-bit product's halves and mixing the
+// high halves with words 1 and 3 and the key; the key is bumped by the two
+// Weyl constants between rounds. The key is the same in every lane, so its
+// schedule stays in scalar registers.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Dropout bytes of one query row for the 32 keys k0 .. k0 + 31 (k0 a
+// multiple of 32) in the 32x32 accumulator layout where lane l owns query
+// column l % 32 and the keys 8 q + 4 (l / 32) + e, q, e = 0..3. The contract:
+// the 16 keys 16 g .. 16 g + 15 of row i use the four words of one Philox
+// call with counter (g, i, head, offset), key j taking byte j mod 16 (byte n
+// = bits 8 (n mod 4) .. +7 of word n / 4). Lane l computes the call for
+// group k0 / 16 + l / 32 and swaps the words its partner lane l ^ 32 needs:
+// word q of the result holds the bytes of keys 8 q + 4 (l / 32) + 0..3.
+__device__ __forceinline__ u32x4 dropout_bytes_32keys(uint32_t key0, uint32_t row, uint32_t head, uint32_t offset,
+                                                      uint32_t seed_lo, uint32_t seed_hi, int half) {
+  const u32x4 w = philox4x32_10(key0 / 16 + (uint32_t)half, row, head, offset, seed_lo, seed_hi);
+  // v_permlane32_swap(x, y): lanes 0-31 get {x[l], x[l + 32]}, lanes 32-63 {y[l - 32], y[l]}
+  const auto s01 = __builtin_amdgcn_permlane32_swap(w[0], w[1], false, false);
+  const auto s23 = __builtin_amdgcn_permlane32_swap(w[2], w[3], false, false);
+  return u32x4{s01[0], s23[0], s01[1], s23[1]};
+}
+
+// Is the byte for accumulator register r (key 8 (r / 4) + 4 half + r % 4) below t?
+__device__ __forceinline__ bool dropout_keep(const u32x4& bytes, int r, uint32_t t) {
+  return ((bytes[r >> 2] >> (8 * (r & 3))) & 0xFFu) < t;
+}
+
 // Workgroup index remap so that consecutive logical tiles share one XCD.
 // Hardware deals workgroups round-robin over the 8 XCDs (id % 8); logical
 // tile t is placed on XCD t / ceil-share, which keeps the tiles of one head

@@ -39,6 +39,12 @@
 //   * exponentials are exp2 with scale*log2(e) folded into one FMA; the row
 //     sum adds the fp32 probabilities, so the saved log-sum-exp keeps fp32
 //     accuracy for the backward.
+//   * dropout (the DROP instantiations): probabilities are dropped after the
+//     row sum and before the product with V (zerotofrontier "Efficient
+//     attention: memory-bound", section "Real code moves even more", places
+//     dropout there in a training forward pass). Each lane draws the Philox
+//     bytes of its row for one 16-key group per 32-key block and swaps half
+//     of them with its partner lane; the 256 / t rescale rides on 1 / l.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -68,9 +74,10 @@ constexpr float kRescaleSlack = 8.f;
 
 }  // namespace
 
-template <int D, bool CAUSAL, bool WIN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_kernel(FwdArgs a) {
   static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
+  static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
   using C = FwdCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, NT = C::NT, CH = C::CH, LOADS = C::LOADS;
   constexpr int KPITCH = C::KPITCH, VPITCH = C::VPITCH, KTILE = C::KTILE, VTILE = C::VTILE;
@@ -240,20 +247,30 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
     bf16x8 pb[KB * 2];
     float lsum = 0.f;
 #pragma unroll
-    for (int kb_i = 0; kb_i < KB; ++kb_i)
+    for (int kb_i = 0; kb_i < KB; ++kb_i) {
+      // dropout: the row sum takes every probability, the product with V only the kept ones
+      u32x4 zb{};
+      if constexpr (DROP)
+        zb = dropout_bytes_32keys((uint32_t)(j * BC + kb_i * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+                                  a.drop.seed_lo, a.drop.seed_hi, half);
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         uint32_t pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * hs + 2 * e;
-          const float p0 = exp2_fast(fmaf(s_cur[kb_i][r], a.c, -m_ref));
-          const float p1 = exp2_fast(fmaf(s_cur[kb_i][r + 1], a.c, -m_ref));
+          float p0 = exp2_fast(fmaf(s_cur[kb_i][r], a.c, -m_ref));
+          float p1 = exp2_fast(fmaf(s_cur[kb_i][r + 1], a.c, -m_ref));
           lsum += p0 + p1;
+          if constexpr (DROP) {
+            if (!dropout_keep(zb, r, a.drop.t)) p0 = 0.f;
+            if (!dropout_keep(zb, r + 1, a.drop.t)) p1 = 0.f;
+          }
           pw[e] = pack_bf16x2(p0, p1);
         }
         pb[kb_i * 2 + hs] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
       }
+    }
     __builtin_amdgcn_iglp_opt(2);
     // stage B: O^T[d, query] += V^T[d, key] P^T[key, query], 16 keys per step
     const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
@@ -317,7 +334,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   }
 
   const float l_tot = pair_sum32(l);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if constexpr (DROP) inv *= a.drop.inv_keep;   // kept probabilities are scaled by 256 / t
   if (qrow < a.Tq) {
     uint16_t* dst = a.o + qoff + (size_t)qrow * D;
 #pragma unroll
@@ -334,12 +352,12 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   }
 }
 
-template <int D, bool CAUSAL, bool WIN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
 static hipError_t launch_fwd(FwdArgs a, hipStream_t stream) {
   using C = FwdCfg<D>;
   a.n_qtiles = (a.Tq + C::BR - 1) / C::BR;
   const uint32_t n = (uint32_t)a.n_qtiles * (uint32_t)(a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WIN>), dim3(n), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WIN, DROP>), dim3(n), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -347,6 +365,10 @@ int fwd_rows_per_workgroup(int d) { return d == 128 ? FwdCfg<128>::BR : FwdCfg<6
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
   if (a.window > 0) return d == 64 ? launch_fwd<64, true, true>(a, stream) : launch_fwd<128, true, true>(a, stream);
+  if (a.drop.t != 0) {
+    if (d == 64) return causal ? launch_fwd<64, true, false, true>(a, stream) : launch_fwd<64, false, false, true>(a, stream);
+    return causal ? launch_fwd<128, true, false, true>(a, stream) : launch_fwd<128, false, false, true>(a, stream);
+  }
   if (d == 64) return causal ? launch_fwd<64, true>(a, stream) : launch_fwd<64, false>(a, stream);
   return causal ? launch_fwd<128, true>(a, stream) : launch_fwd<128, false>(a, stream);
 }

@@ -8,6 +8,15 @@
 
 namespace fa {
 
+// Dropout of the attention probabilities: P_ij is kept iff its Philox byte is
+// below t (keep probability t / 256) and kept entries are scaled by 256 / t.
+struct DropArgs {
+  uint32_t t;               // keep threshold in [1, 256]; 0: no dropout
+  uint32_t seed_lo, seed_hi;
+  uint32_t offset;
+  float inv_keep;           // 256 / t
+};
+
 struct FwdArgs {
   const uint16_t* q;  // [B,Hq,Tq,d] bf16
   const uint16_t* k;  // [B,Hkv,Tk,d] bf16
@@ -18,6 +27,7 @@ struct FwdArgs {
   float c;            // scale * log2(e)
   int n_qtiles;       // filled in by the launcher
   int window;         // causal band of this many keys (0: plain mask)
+  DropArgs drop;
 };
 
 struct Fp8Args {
@@ -76,6 +86,7 @@ struct BwdArgs {
   float scale;
   float c;                  // scale * log2(e)
   int window;               // causal band of this many keys (0: plain mask)
+  DropArgs drop;
 };
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);

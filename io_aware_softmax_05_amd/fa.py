@@ -33,6 +33,8 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _S = ctypes.c_size_t
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
 
 # (restype, argtypes) per exported symbol, in header order.
 _SIGNATURES = {
@@ -44,6 +46,10 @@ _SIGNATURES = {
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_dropout_keep_threshold": (_I, [_F]),
+    "fa_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _P]),
+    "fa_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I,
+                            _F, _U64, _U32, _P]),
     "fa_decode_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
@@ -166,6 +172,31 @@ def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq,
                                       _ptr(dk), _ptr(dv), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tq, Tk, d,
                                       float(scale), int(window), _stream(stream))
     _check(st, "fa_bwd_window")
+
+
+def fa_dropout_keep_threshold(p_drop) -> int:
+    """Keep threshold t in [1, 256] for p_drop (raises FaError when unusable)."""
+    t = int(load_library().fa_dropout_keep_threshold(float(p_drop)))
+    if t < 0:
+        raise FaError(t, "fa_dropout_keep_threshold")
+    return t
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, p_drop, seed, offset,
+                   stream=None) -> None:
+    st = load_library().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
+                                       float(scale), int(bool(causal)), float(p_drop), int(seed), int(offset),
+                                       _stream(stream))
+    _check(st, "fa_fwd_dropout")
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, causal,
+                   p_drop, seed, offset, stream=None) -> None:
+    st = load_library().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tq, Tk, d,
+                                       float(scale), int(bool(causal)), float(p_drop), int(seed), int(offset),
+                                       _stream(stream))
+    _check(st, "fa_bwd_dropout")
 
 
 def fa_decode_workspace_size(B, Hq, Tk_max, d) -> int:

@@ -173,6 +173,19 @@ def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, window: int = 
     return o, lse
 
 
+def attention_fwd_head_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows, dropout=None):
+    """O [n,d] and LSE [n] of some query rows of one (batch, query head), from
+    the full tensors, so that the dropout stream sees the head's own index
+    b * Hq + h. Same computation as attention_fwd."""
+    Hq, Hkv = np.shape(q)[1], np.shape(k)[1]
+    hk = _kv_head(h, Hq, Hkv)
+    kk = np.asarray(k[b, hk], dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    p, lse = row_probs(np.asarray(q[b, h], dtype=np.float64)[rows], kk, scale, rows, np.shape(q)[2], causal)
+    pd, _ = _dropped(p, dropout, b * Hq + h, rows, kk.shape[0])
+    return pd @ np.asarray(v[b, hk], dtype=np.float64), lse
+
+
 def e4m3_to_f64(bits) -> np.ndarray:
     """Values of OCP 8-bit floats in the E4M3 format, exactly, as fp64.
 

@@ -189,3 +189,37 @@ def test_fp8_forward_rejects_bad_arguments():
     for name, args in bad.items():
         assert L.fa_fwd_fp8(*args) == fa.FA_ERR_INVALID_ARG, name
     assert L.fa_fwd_fp8(*ok[:13], 48, *ok[14:]) == fa.FA_ERR_UNSUPPORTED   # d
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.25, 0.5, 0.9, 1.0 / 512, 3.0 / 512, 0.998, 0.3333])
+def test_dropout_keep_threshold_matches_the_oracle(p):
+    from oracle import attention_ref as ref
+    # the library takes p as fp32; the oracle's rule is applied to that same value
+    p32 = float(ctypes.c_float(p).value)
+    assert fa.fa_dropout_keep_threshold(p) == ref.keep_threshold(p32)
+
+
+@pytest.mark.parametrize("p", [1.0, -0.01, 0.999, float("nan"), float("inf")])
+def test_dropout_keep_threshold_rejects(p):
+    assert lib().fa_dropout_keep_threshold(p) == fa.FA_ERR_INVALID_ARG
+    with pytest.raises(fa.FaError):
+        fa.fa_dropout_keep_threshold(p)
+
+
+def test_dropout_entry_points_check_like_the_plain_ones():
+    common = (1, 2, 1, 8, 8, 64, 0.125, 1)
+    # an unusable dropout probability is refused before anything else is looked at
+    for p in (1.0, -0.5, float("nan")):
+        assert lib().fa_fwd_dropout(A, A, A, A, None, *common, p, 1, 0, None) == fa.FA_ERR_INVALID_ARG
+        assert lib().fa_bwd_dropout(A, A, A, A, A, A, A, A, A, A, 1 << 20, *common, p, 1, 0, None) \
+            == fa.FA_ERR_INVALID_ARG
+    # with a usable one, the plain entry points' checks apply
+    assert lib().fa_fwd_dropout(None, A, A, A, None, *common, 0.1, 1, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert lib().fa_fwd_dropout(A, A, A, A, None, 1, 2, 1, 8, 8, 96, 0.125, 1, 0.1, 1, 0, None) \
+        == fa.FA_ERR_UNSUPPORTED
+    assert lib().fa_fwd_dropout(A, A, A, MIS, None, *common, 0.1, 1, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert lib().fa_bwd_dropout(A, A, A, A, A, A, A, A, A, A, 0, *common, 0.1, 1, 0, None) == fa.FA_ERR_WORKSPACE
+    assert lib().fa_bwd_dropout(A, A, A, A, A, None, A, A, A, A, 1 << 20, *common, 0.1, 1, 0, None) \
+        == fa.FA_ERR_INVALID_ARG
+    assert lib().fa_bwd_dropout(A, A, A, A, A, A, A, A, A, A, 1 << 20, 1, 3, 2, 8, 8, 64, 0.125, 1, 0.1, 1, 0,
+                                None) == fa.FA_ERR_INVALID_ARG

@@ -203,7 +203,7 @@ def test_dropped_backward_finite_differences(causal, Hq, Hkv, m=ref):
         np.testing.assert_allclose(gx, num, rtol=1e-6, atol=1e-8)
 
 
-def test_dropped_sampled_gradients_match_full():
+def test_dropped_sampled_rows_and_gradients_match_full():
     Hq, Hkv, T, d = 4, 2, 40, 8
     q, k, v, do = _rand(15, 2, Hq, T, d), _rand(16, 2, Hkv, T, d), _rand(17, 2, Hkv, T, d), _rand(18, 2, Hq, T, d)
     drop = ref.Dropout(t=230, seed=31337, offset=5)
@@ -212,6 +212,10 @@ def test_dropped_sampled_gradients_match_full():
         rows = np.array([0, 17, 39])
         np.testing.assert_allclose(ref.attention_bwd_dq_rows(q, k, v, do, 0.4, causal, 1, 3, rows, dropout=drop),
                                    dq[1, 3, rows], rtol=1e-12, atol=1e-12)
+        o, lse = ref.attention_fwd(q, k, v, 0.4, causal, dropout=drop)
+        ho, hl = ref.attention_fwd_head_rows(q, k, v, 0.4, causal, 1, 3, rows, dropout=drop)
+        np.testing.assert_allclose(ho, o[1, 3, rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(hl, lse[1, 3, rows], rtol=1e-12, atol=1e-12)
         keys = np.array([2, 20, 39])
         sk, sv = ref.attention_bwd_dkdv_keys(q, k, v, do, 0.4, causal, 1, 1, keys, dropout=drop)
         np.testing.assert_allclose(sk, dk[1, 1, keys], rtol=1e-12, atol=1e-12)
