@@ -220,6 +220,12 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   // LDS ring: iteration j reads K_{j+1} from kbuf[(j+1)&1] and V_j from
   // vbuf[j&1]; it refills kbuf[j&1] with K_{j+2} and vbuf[(j+1)&1] with V_{j+1}.
   f32x16 s_a[KB], s_b[KB];
+  // Dropout: the Philox bytes of this lane's row for the 32-key blocks of a tile.
+  u32x4 z_a[KB], z_b[KB];
+  auto drop_bytes = [&](int j, int kb_i) -> u32x4 {
+    return dropout_bytes_32keys((uint32_t)(j * BC + kb_i * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+                                a.drop.seed_lo, a.drop.seed_hi, half);
+  };
   const int j0 = j_begin;
   if (j0 < n_kv) {
     load_k(j0);
@@ -230,6 +236,10 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
     store_k((j0 + 1) & 1);
     __syncthreads();
     scores(j0 & 1, s_a);
+    if constexpr (DROP) {   // dropout bytes of the first tile; later tiles draw theirs a tile ahead
+#pragma unroll
+      for (int kb_i = 0; kb_i < KB; ++kb_i) z_a[kb_i] = drop_bytes(j0, kb_i);
+    }
     if (j0 >= n_full || j0 < j_head) mask(j0, s_a);
     m = rowmax(s_a) * a.c;   // l and u are still zero: nothing to rescale
     __syncthreads();         // every wave has read K_j0 before K_j0+2 replaces it
@@ -237,7 +247,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
 
   // Tile j (s_cur = S_j, masked; m covers it): P_j and O += V_j P_j, while
   // S_{j+1} goes to s_nxt, is masked if needed, and its row max moves m.
-  auto body = [&](int j, auto next_masked, auto has_next, f32x16* s_cur, f32x16* s_nxt) {
+  auto body = [&](int j, auto next_masked, auto has_next, f32x16* s_cur, f32x16* s_nxt, u32x4* z_cur,
+                  u32x4* z_nxt) {
     constexpr bool HN = decltype(has_next)::value;
     load_k(j + 2);
     load_v(j + 1);
@@ -249,10 +260,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
 #pragma unroll
     for (int kb_i = 0; kb_i < KB; ++kb_i) {
       // dropout: the row sum takes every probability, the product with V only the kept ones
-      u32x4 zb{};
-      if constexpr (DROP)
-        zb = dropout_bytes_32keys((uint32_t)(j * BC + kb_i * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
-                                  a.drop.seed_lo, a.drop.seed_hi, half);
+      const u32x4 zb = z_cur[kb_i];
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         uint32_t pw[4];
@@ -286,6 +294,11 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
           oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kb_i * 2 + hs], oacc[db]);
         }
       }
+    // the next tile's dropout bytes, drawn while the matrix cores run O += V_j P_j
+    if constexpr (DROP && HN) {
+#pragma unroll
+      for (int kb_i = 0; kb_i < KB; ++kb_i) z_nxt[kb_i] = drop_bytes(j + 1, kb_i);
+    }
     l += lsum;
     if constexpr (HN) {
       if constexpr (decltype(next_masked)::value) mask(j + 1, s_nxt);
@@ -313,24 +326,24 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   int j = j0;
   if constexpr (WIN) {   // the window's first tiles: masked, one at a time
     for (; j + 1 < j_head; ++j) {
-      body(j, std::true_type{}, std::true_type{}, s_a, s_b);
+      body(j, std::true_type{}, std::true_type{}, s_a, s_b, z_a, z_b);
 #pragma unroll
       for (int kb_i = 0; kb_i < KB; ++kb_i) s_a[kb_i] = s_b[kb_i];
     }
   }
   for (; j + 2 < n_full; j += 2) {
-    body(j, std::false_type{}, std::true_type{}, s_a, s_b);
-    body(j + 1, std::false_type{}, std::true_type{}, s_b, s_a);
+    body(j, std::false_type{}, std::true_type{}, s_a, s_b, z_a, z_b);
+    body(j + 1, std::false_type{}, std::true_type{}, s_b, s_a, z_b, z_a);
   }
   for (; j + 2 < n_kv; j += 2) {
-    body(j, std::true_type{}, std::true_type{}, s_a, s_b);
-    body(j + 1, std::true_type{}, std::true_type{}, s_b, s_a);
+    body(j, std::true_type{}, std::true_type{}, s_a, s_b, z_a, z_b);
+    body(j + 1, std::true_type{}, std::true_type{}, s_b, s_a, z_b, z_a);
   }
   if (j + 1 < n_kv) {
-    body(j, std::true_type{}, std::true_type{}, s_a, s_b);
-    body(j + 1, std::true_type{}, std::false_type{}, s_b, s_a);
+    body(j, std::true_type{}, std::true_type{}, s_a, s_b, z_a, z_b);
+    body(j + 1, std::true_type{}, std::false_type{}, s_b, s_a, z_b, z_a);
   } else if (j < n_kv) {
-    body(j, std::true_type{}, std::false_type{}, s_a, s_b);
+    body(j, std::true_type{}, std::false_type{}, s_a, s_b, z_a, z_b);
   }
 
   const float l_tot = pair_sum32(l);
