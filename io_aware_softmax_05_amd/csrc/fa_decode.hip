@@ -13,7 +13,8 @@
 // few single-wave workgroups per compute unit. Each wave streams the tiles of
 // its items back to back through a three-stage ring of direct-to-LDS loads,
 // so two 32-key K/V tiles are always in flight, also across item
-// boundaries. The query heads that share a KV head are the rows of one
+// boundaries. The cache is read exactly once, so its loads carry the
+// non-temporal hint. The query heads that share a KV head are the rows of one
 // 16-row MFMA tile, so every cached key and value is read from HBM once. Per
 // item the wave runs the online-softmax recurrence and stores the partial
 // state (m, l, u).
@@ -139,9 +140,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + tile0, bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + tile0, bytes);
 #pragma unroll
-    for (int i = 0; i < C::DMA; ++i) {
-      dma_b128(krs, st + i * 1024, dma_off[i]);
-      dma_b128(vrs, st + TILE + i * 1024, dma_off[i]);
+    for (int i = 0; i < C::DMA; ++i) {   // each cached row is read once: non-temporal loads
+      dma_b128_stream(krs, st + i * 1024, dma_off[i]);
+      dma_b128_stream(vrs, st + TILE + i * 1024, dma_off[i]);
     }
     if (live && ld.t == 0) {
       // first tile of an item: its query rows come along (unswizzled); a wait
