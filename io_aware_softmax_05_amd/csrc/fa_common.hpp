@@ -187,6 +187,18 @@ __device__ __forceinline__ bool dropout_keep(const u32x4& bytes, int r, uint32_t
   return ((bytes[r >> 2] >> (8 * (r & 3))) & 0xFFu) < t;
 }
 
+// Compensated (Kahan) summation: s accumulates, c carries the rounding error
+// of each addition with its sign flipped, and s - c is the sum. A row of
+// millions of keys adds one tile partial at a time to a running sum that can
+// be far larger than each partial (after a dominant early key, for instance);
+// plain fp32 addition would lose up to 2^-24 of the sum per tile.
+__device__ __forceinline__ void kahan_add(float& s, float& c, float x) {
+  const float y = x - c;
+  const float t = s + y;
+  c = (t - s) - y;
+  s = t;
+}
+
 // Workgroup index remap so that consecutive logical tiles share one XCD.
 // Hardware deals workgroups round-robin over the 8 XCDs (id % 8); logical
 // tile t is placed on XCD t / ceil-share, which keeps the tiles of one head

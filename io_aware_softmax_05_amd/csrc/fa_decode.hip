@@ -323,20 +323,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   __syncthreads();
   const float mstar = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
 
-  float lsum = 0.f, acc[PER];
+  float lsum = 0.f, lcomp = 0.f, acc[PER];   // lsum - lcomp: compensated sum over thousands of splits
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
 #pragma unroll 4
   for (int s = wave; s < n_used; s += 4) {
     const float w = exp2_fast(a.part_m[base + s] - mstar);
-    lsum = fmaf(w, a.part_l[base + s], lsum);
+    kahan_add(lsum, lcomp, w * a.part_l[base + s]);
     const float* u = a.part_u + (base + s) * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, u[e], acc[e]);
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) red_u[wave][lane * PER + e] = acc[e];
-  if (lane == 0) red_u[wave][D] = lsum;
+  if (lane == 0) red_u[wave][D] = lsum - lcomp;
   __syncthreads();
   if (wave != 0) return;
   const float l_tot = red_u[0][D] + red_u[1][D] + red_u[2][D] + red_u[3][D];

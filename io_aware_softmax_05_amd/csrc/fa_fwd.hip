@@ -142,6 +142,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m = -INFINITY;   // running max of scaled scores, log2 units
   float l = 0.f;         // this lane's partial running sum
+  float lc = 0.f;        // its compensation (l - lc is the sum)
 
   // This thread's share of a tile: LOADS 16-byte chunks (row, chunk).
   uint32_t g_off[LOADS], k_lds[LOADS], v_lds[LOADS];
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
 #pragma unroll
       for (int kb_i = 0; kb_i < KB; ++kb_i) z_nxt[kb_i] = drop_bytes(j + 1, kb_i);
     }
-    l += lsum;
+    kahan_add(l, lc, lsum);
     if constexpr (HN) {
       if constexpr (decltype(next_masked)::value) mask(j + 1, s_nxt);
       const float m_new = fmaxf(m, rowmax(s_nxt) * a.c);
@@ -310,6 +311,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
         // move the reference: l and u are rescaled together (after O += V_j P_j)
         const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
         l *= alpha;
+        lc *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
     body(j, std::true_type{}, std::false_type{}, s_a, s_b, z_a, z_b);
   }
 
-  const float l_tot = pair_sum32(l);
+  const float l_tot = pair_sum32(l - lc);
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if constexpr (DROP) inv *= a.drop.inv_keep;   // kept probabilities are scaled by 256 / t
   if (qrow < a.Tq) {

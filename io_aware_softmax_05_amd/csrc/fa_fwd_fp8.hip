@@ -130,6 +130,7 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m = -INFINITY;   // reference maximum of the scaled scores, log2 units
   float l = 0.f;         // this lane's partial running sum of P'
+  float lc = 0.f;        // its compensation (l - lc is the sum)
 
   // This thread's chunk of each tile: K row kr, chunk kc; V^T row vr, chunk vc.
   const int kr = tid / C::KCH, kc = tid % C::KCH;
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
     __builtin_amdgcn_iglp_opt(0);
     // stage B: O'^T[d, query] += V^T[d, key] P'^T[key, query]
     pv(j & 1, pb);
-    l += lsum;
+    kahan_add(l, lc, lsum);
     if constexpr (HN) {
       if constexpr (decltype(next_masked)::value) mask(j + 1, s_nxt);
       const float m_new = fmaxf(m, rowmax(s_nxt) * c);
@@ -251,6 +252,7 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
         // move the reference: l and u are rescaled together (after O' += V_j P'_j)
         const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
         l *= alpha;
+        lc *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
     body(j, std::true_type{}, std::false_type{}, s_a, s_b);
   }
 
-  const float l_tot = pair_sum32(l);
+  const float l_tot = pair_sum32(l - lc);
   const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
   if (qrow < a.Tq) {
     uint16_t* dst = a.o + (size_t)bh * a.Tq * D + (size_t)qrow * D;

@@ -181,7 +181,9 @@ def attention_fwd_head_rows(q, k, v, scale: float, causal: bool, b: int, h: int,
     hk = _kv_head(h, Hq, Hkv)
     kk = np.asarray(k[b, hk], dtype=np.float64)
     rows = np.asarray(rows, dtype=np.int64)
-    p, lse = row_probs(np.asarray(q[b, h], dtype=np.float64)[rows], kk, scale, rows, np.shape(q)[2], causal)
+    # the sampled rows are taken before widening (a head may hold millions of rows)
+    p, lse = row_probs(np.asarray(np.asarray(q[b, h])[rows], dtype=np.float64), kk, scale, rows, np.shape(q)[2],
+                       causal)
     pd, _ = _dropped(p, dropout, b * Hq + h, rows, kk.shape[0])
     return pd @ np.asarray(v[b, hk], dtype=np.float64), lse
 
@@ -254,16 +256,16 @@ def attention_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: in
                           dropout=None):
     """dQ for some query rows of one (batch, query head): each row's gradient
     needs only that row's own scores, so it can be evaluated at any size."""
-    q = np.asarray(q[b, h], dtype=np.float64)
     Hq, Hkv = np.shape(do)[1], np.shape(k)[1]
     hk = _kv_head(h, Hq, Hkv)
     kk = np.asarray(k[b, hk], dtype=np.float64)
     vv = np.asarray(v[b, hk], dtype=np.float64)
     rows = np.asarray(rows, dtype=np.int64)
-    Tq = q.shape[0]
-    p, _ = row_probs(q[rows], kk, scale, rows, Tq, causal, window)
+    Tq = np.shape(q)[2]
+    # the sampled rows are taken before widening (a head may hold millions of rows)
+    p, _ = row_probs(np.asarray(np.asarray(q[b, h])[rows], dtype=np.float64), kk, scale, rows, Tq, causal, window)
     _, z = _dropped(p, dropout, b * Hq + h, rows, kk.shape[0])
-    g = np.asarray(do[b, h], dtype=np.float64)[rows]
+    g = np.asarray(np.asarray(do[b, h])[rows], dtype=np.float64)
     dp = (g @ vv.T) * z
     ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     return scale * (ds @ kk)
