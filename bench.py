@@ -30,9 +30,9 @@ written by `--record-traffic DIR` from four rocprofv3 counter runs:
     DIR/write_copy  rocprofv3 --pmc WRITE_SIZE -- (same)
 (each with --output-format csv -d DIR/<name> -o run). Each counter is scaled
 by the ratio of the known copy size to what that counter reads for the plain
-1 GiB device copy. The file records a hash of the kernel sources; when the
-sources change, the traffic is reported as null until the counters are taken
-again.
+1 GiB device copy. Each unit records a hash of the sources its kernels are
+built from (plus the shared headers); when those change, that unit's traffic is
+reported as null until the counters are taken again.
 """
 from __future__ import annotations
 
@@ -95,14 +95,33 @@ def fwd_flops(B, Hq, Tq, Tk, d, causal):
     return 4.0 * d * pairs * B * Hq
 
 
-def source_hash() -> str:
+# Source file of each kernel family; every kernel also depends on the shared headers.
+KERNEL_SOURCES = {"fwd_bf16_kernel": "fa_fwd.hip", "fwd_fp8_kernel": "fa_fwd_fp8.hip",
+                  "bwd_dq_kernel": "fa_bwd.hip", "bwd_dkdv_kernel": "fa_bwd.hip",
+                  "decode_split_kernel": "fa_decode.hip", "decode_merge_kernel": "fa_decode.hip"}
+SHARED_SOURCES = ("fa_common.hpp", "fa_internal.h")
+
+
+def source_hash(files=None) -> str:
+    """sha256 over the named kernel sources (all of them when None)."""
+    if files is None:
+        paths = [p for p in glob.glob(os.path.join(CSRC, "*")) if p.endswith((".hip", ".hpp", ".h", ".cpp"))]
+    else:
+        paths = [os.path.join(CSRC, f) for f in files]
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if p.endswith((".hip", ".hpp", ".h", ".cpp")):
-            h.update(os.path.basename(p).encode())
-            with open(p, "rb") as f:
-                h.update(f.read())
+    for p in sorted(paths):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
+
+
+def unit_source_hash(unit: str) -> str:
+    """Hash of the sources the kernels of a traffic unit are built from."""
+    files = set(SHARED_SOURCES)
+    for spec in TRAFFIC_UNITS[unit]:
+        files.add(KERNEL_SOURCES[spec.split("<")[0]])
+    return source_hash(sorted(files))
 
 
 def recorded_traffic(unit: str):
@@ -113,10 +132,10 @@ def recorded_traffic(unit: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_hash():
-        return None
     u = rec.get("units", {}).get(unit)
-    return None if u is None else float(u["bytes"])
+    if u is None or unit not in TRAFFIC_UNITS or u.get("source_sha256") != unit_source_hash(unit):
+        return None
+    return float(u["bytes"])
 
 
 # ------------------------------------------------------------------ GPU timing
@@ -479,8 +498,8 @@ def record_traffic(d):
             nk = hits[0]
             ks[f"{nk[0]} grid {nk[1]}"] = {"fetch_kib": round(fetch[nk], 1), "write_kib": round(write.get(nk, 0.0), 1)}
             total += fetch[nk] * 1024 * f_fac + write.get(nk, 0.0) * 1024 * w_fac
-        units[unit] = {"bytes": round(total), "kernels": ks}
-    rec = {"source_sha256": source_hash(),
+        units[unit] = {"bytes": round(total), "source_sha256": unit_source_hash(unit), "kernels": ks}
+    rec = {"source_sha256": source_hash(),   # all kernel sources; each unit also records its own
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
            "units": units}

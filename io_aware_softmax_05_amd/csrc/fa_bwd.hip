@@ -475,6 +475,15 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   // tiles before j_begin are invisible to every row of the workgroup
   const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
 
+  // Dropout: the Philox bytes of this lane's row for the 32-key blocks of the
+  // current tile (the forward's layout and contract); the next tile's are
+  // drawn while the matrix cores run this tile's dQ product.
+  u32x4 zcur[KB];
+  auto drop_bytes = [&](int j, int kb) -> u32x4 {
+    return dropout_bytes_32keys((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+                                a.drop.seed_lo, a.drop.seed_hi, half);
+  };
+
   auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) {
     const FA_LDS uint8_t* kt = st;
     const FA_LDS uint8_t* vt = st + KTILE;
@@ -491,10 +500,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     uint32_t dsw[KB][8];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      u32x4 zb{};   // dropout bytes of this row's 32 keys (the forward's layout and contract)
-      if constexpr (DROP)
-        zb = dropout_bytes_32keys((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
-                                  a.drop.seed_lo, a.drop.seed_hi, half);
+      const u32x4 zb = zcur[kb];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0 = exp2_fast(fmaf(s[kb][r], a.c, -lse2));
@@ -527,10 +533,18 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
           dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
         }
       }
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j + 1, kb);
+    }
   };
 
   // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
   constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
+  if constexpr (DROP) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
+  }
   if (j_begin < n_kv) {
     for (int st = 0; st < C::NSTAGE - 1; ++st) issue(j_begin + st, st);
     wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
