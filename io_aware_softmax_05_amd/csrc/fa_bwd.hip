@@ -53,12 +53,14 @@ struct DkdvCfg {
   static constexpr int ROWB = 2 * D;                 // LDS bytes per row (swizzled, unpadded)
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int QTILE = BQ * ROWB;            // one Q (or dO) tile
-  static constexpr int STATS = BQ * 8;               // (lse2, D) per row
+  // row statistics: the lse2 plane, then the -D plane, each in whole 256-byte wave loads
+  static constexpr int SLOT = (BQ * 4 + 255) / 256 * 256;
+  static constexpr int STATS = 2 * SLOT;
   static constexpr int STAGE = 2 * QTILE + STATS;
   static constexpr int NSTAGE = NSTAGE_;
   static constexpr int TILE_DMA = 2 * BQ * CH / 64;  // 128-bit wave loads per tile (Q and dO)
   static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
-  static constexpr int STAT_DMA = BQ * 2 / 64;       // 32-bit wave loads of the statistics
+  static constexpr int STAT_DMA = STATS / 256;       // 32-bit wave loads of the statistics
   static constexpr int VM_PER_TILE = DMA_PER_WAVE + STAT_DMA;
   static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
 };
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
     dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
   }
-  const int st_row = lane >> 1;                   // stats loads: (row, lse2 or D)
+  const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
 
   // Tile iterator for the loads (two tiles ahead of the compute).
   int ld_it = 0, ld_h = 0, ld_qi = qt_begin;
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats + rows * 2, (uint32_t)a.Tq * 8);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.stats + rows, (uint32_t)a.Tq * 4);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.stats + plane + rows, (uint32_t)a.Tq * 4);
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
       const bool ok = live && q0 + (int)dma_row[i] < a.Tq;
@@ -169,8 +172,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     }
 #pragma unroll
     for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
-      const bool sok = live && q0 + 32 * i + st_row < a.Tq;
-      dma_b32(srs, st + 2 * QTILE + 256 * i, sok ? (uint32_t)((q0 + 32 * i) * 2 + lane) * 4 : kOutOfRange);
+      constexpr int PER_PLANE = C::STAT_DMA / 2;
+      const int pl = i / PER_PLANE, row = 64 * (i % PER_PLANE) + lane;
+      const bool sok = live && row < BQ && q0 + row < a.Tq;   // other lanes write zeros inside the slot
+      dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE),
+              sok ? (uint32_t)(q0 + row) * 4 : kOutOfRange);
     }
     ++ld_it;
     if (++ld_qi == n_qt) {
@@ -197,15 +203,30 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     const FA_LDS uint8_t* stt = st + 2 * QTILE;
     const uint32_t bhq = (uint32_t)(b * a.Hq + hk * G + head);   // flattened query head (dropout stream)
     // S = Q K^T and dP = dO V^T for BQ queries x 32 keys (one key per lane).
+    // On unmasked tiles without dropout the dP product starts from -D
+    // (accumulator register r of block qb holds row 32 qb + 8 (r / 4) +
+    // 4 half + r % 4, so four -D values of consecutive rows fill registers
+    // 4 g4 .. 4 g4 + 3), and dP - D comes out of the matrix cores; masked
+    // tiles (fewer, and short of registers) and dropout add -D afterwards.
+    constexpr bool FOLD = !DROP && !decltype(masked)::value;
     f32x16 s[QB], dp[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      f32x16 dinit{};
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 nd = *(const FA_LDS f32x4*)(stt + C::SLOT + (qb * 32 + 8 * g4 + 4 * half) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dinit[4 * g4 + e] = nd[e];
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t off = qb * 32 * ROWB + (q_rd ^ (32 * ks));
-        // the first products start from an inline zero (no register clearing)
+        // the first products start from an inline zero (no register clearing) or from -D
         s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], ks == 0 ? f32x16{} : s[qb]);
-        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? f32x16{} : dp[qb]);
+        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? dinit : dp[qb]);
       }
     }
     // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
@@ -230,10 +251,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int rq = qb * 32 + 8 * g4 + 4 * half;
-        const f32x4 s01 = *(const FA_LDS f32x4*)(stt + rq * 8);
-        const f32x4 s23 = *(const FA_LDS f32x4*)(stt + rq * 8 + 16);
-        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+        const f32x4 l2 = *(const FA_LDS f32x4*)(stt + rq * 4);   // lse2 of rows rq .. rq + 3
+        f32x4 nd{};                                               // their -D, unless folded into dP
+        if constexpr (!FOLD) nd = *(const FA_LDS f32x4*)(stt + C::SLOT + rq * 4);
         float p[4], ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -243,15 +263,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
             const int dist = dbase + (qb * 32 + 8 * g4 + e);   // one unsigned compare for the band
             if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
           }
-          float dpe = dp[qb][r];
+          float dpe = dp[qb][r];   // dP - D when folded, else dP
           float pv = pe;
           if constexpr (DROP) {   // dV takes the kept P; dP is dropped and rescaled
             const bool keep = zbyte[r] < a.drop.t;
             pv = keep ? pe : 0.f;
             dpe = keep ? dpe * a.drop.inv_keep : 0.f;
           }
+          if constexpr (!FOLD) dpe += nd[e];
           p[e] = pv;
-          ds[e] = pe * (dpe - dl[e]);
+          ds[e] = pe * dpe;
         }
         pw[qb][2 * g4] = pack_bf16x2(p[0], p[1]);
         pw[qb][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
@@ -428,7 +449,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     // rows past Tq: Q = dO = 0, so dS = 0 whatever lse2 holds
     const float lse = live ? a.lse[qoff + qrow] : 0.f;
     lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-    if (live && half == 0) *(float2*)(a.stats + 2 * (qoff + qrow)) = float2{lse2, delta};
+    if (live && half == 0) {   // two planes: lse2 for every row, then -D
+      a.stats[qoff + qrow] = lse2;
+      a.stats[(size_t)a.B * a.Hq * a.Tq + qoff + qrow] = -delta;
+    }
   }
 
   f32x16 dq_acc[D / 32];

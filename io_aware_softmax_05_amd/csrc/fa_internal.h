@@ -81,7 +81,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* stats;             // [B,Hq,Tq,2] workspace: (LSE * log2 e, rowsum(dO * O))
+  float* stats;             // workspace: [B,Hq,Tq] LSE * log2 e, then [B,Hq,Tq] -rowsum(dO * O)
   int B, Hq, Hkv, Tq, Tk;
   float scale;
   float c;                  // scale * log2(e)
