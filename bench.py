@@ -10,10 +10,14 @@ resident in HBM. W untimed steps, then K steps timed between two device
 synchronisations; HIP events recorded around every launch, on the stream the
 kernels run on, give per-launch durations.
 
-After the timed region, in the same run (not part of `value`):
+After the timed region, in the same run (not part of `value`), under "targets":
   * the causal long-context forward (B1 H32 T8192 d128) and split-KV decoding
-    (B16 Hq32 Hkv8, lengths U[4096, 32768] from seed 5, d128) are timed the
-    same way;
+    (B16 Hq32 Hkv8, lengths U[4096, 32768] from seed 5, d128), each the median
+    of 50 launches after 10 untimed;
+  * the causal 32k GQA layer (B1 Hq32 Hkv8 T32768 d128) fwd and bwd, the
+    sliding-window layer (same, W4096) fwd and bwd, the fp8 causal forward
+    (B1 H32 T8192 d128) and the GPT-2-medium layer with dropout p = 0.1 fwd and
+    bwd; the fp32 single-head forward (B1 H1 T256 d64) as a latency;
   * the fp64 CPU oracle is timed on a bounded sample of the step's workload.
 Prints one JSON line.
 
