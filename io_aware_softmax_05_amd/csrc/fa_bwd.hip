@@ -508,6 +508,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
                                 a.drop.seed_lo, a.drop.seed_hi, half);
   };
 
+  // At d = 128 without dropout every dP^T chain starts from a register block
+  // holding -D (one query per lane, so one value), read as the first
+  // product's accumulator input: dP - D comes out of the matrix cores at no
+  // per-tile cost. (d = 64 has no 16 registers to spare at two workgroups per
+  // CU; dropout needs dP itself.)
+  constexpr bool FOLD = D == 128 && !DROP;
+  f32x16 ndelta;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndelta[r] = FOLD ? -delta : 0.f;
+
   auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) {
     const FA_LDS uint8_t* kt = st;
     const FA_LDS uint8_t* vt = st + KTILE;
@@ -518,7 +528,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
       for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
         s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], ks == 0 ? f32x16{} : s[kb]);
-        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? f32x16{} : dp[kb]);
+        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? (FOLD ? ndelta : f32x16{}) : dp[kb]);
       }
     }
     uint32_t dsw[KB][8];
@@ -539,7 +549,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
           dp0 = dropout_keep(zb, r, a.drop.t) ? dp0 * a.drop.inv_keep : 0.f;
           dp1 = dropout_keep(zb, r + 1, a.drop.t) ? dp1 * a.drop.inv_keep : 0.f;
         }
-        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp0 - delta), p1 * (dp1 - delta));
+        const float dsub = FOLD ? 0.f : delta;   // folded: dp already holds dP - D
+        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp0 - dsub), p1 * (dp1 - dsub));
       }
     }
     if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
