@@ -100,9 +100,10 @@ def fwd_flops(B, Hq, Tq, Tk, d, causal):
 
 
 # Source file of each kernel family; every kernel also depends on the shared headers.
-KERNEL_SOURCES = {"fwd_bf16_kernel": "fa_fwd.hip", "fwd_fp8_kernel": "fa_fwd_fp8.hip",
-                  "bwd_dq_kernel": "fa_bwd.hip", "bwd_dkdv_kernel": "fa_bwd.hip",
-                  "decode_split_kernel": "fa_decode.hip", "decode_merge_kernel": "fa_decode.hip"}
+_BWD = ("fa_bwd_kernels.hpp", "fa_bwd.hip", "fa_bwd_window.hip")
+KERNEL_SOURCES = {"fwd_bf16_kernel": ("fa_fwd.hip",), "fwd_fp8_kernel": ("fa_fwd_fp8.hip",),
+                  "bwd_dq_kernel": _BWD, "bwd_dkdv_kernel": _BWD,
+                  "decode_split_kernel": ("fa_decode.hip",), "decode_merge_kernel": ("fa_decode.hip",)}
 SHARED_SOURCES = ("fa_common.hpp", "fa_internal.h")
 
 
@@ -124,7 +125,7 @@ def unit_source_hash(unit: str) -> str:
     """Hash of the sources the kernels of a traffic unit are built from."""
     files = set(SHARED_SOURCES)
     for spec in TRAFFIC_UNITS[unit]:
-        files.add(KERNEL_SOURCES[spec.split("<")[0]])
+        files.update(KERNEL_SOURCES[spec.split("<")[0]])
     return source_hash(sorted(files))
 
 

@@ -21,7 +21,14 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfa_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip",
+           "fa_bwd_window.hip"]
+
+# Per-source options. fa_bwd.hip: MFMAs in VGPR form (the d = 128 backward's
+# default AGPR form copies every S and dP result back for the vector math;
+# measured faster on the causal GQA backward, slower on the window one, which
+# lives in fa_bwd_window.hip).
+SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -42,7 +49,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

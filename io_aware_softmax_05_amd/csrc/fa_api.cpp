@@ -197,7 +197,7 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   a.c = scale * fa::kLog2eHost;
   a.window = window;
   a.drop = drop;
-  return to_status(fa::launch_bwd(a, d, causal != 0, stream));
+  return to_status(window > 0 ? fa::launch_bwd_window(a, d, stream) : fa::launch_bwd(a, d, causal != 0, stream));
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -1,0 +1,643 @@
+// fa_bwd_kernels.hpp -- kernels of the backward pass of exact attention by
+// recomputation, and their launch template. Included by fa_bwd.hip (plain,
+// causal and dropout instantiations) and fa_bwd_window.hip (sliding window),
+// which are compiled with different register-form options.
+//
+// The probabilities are never stored: each kernel rebuilds P tile by tile
+// from Q, K and the fp32 log-sum-exp the forward saved (aimlrounds
+// "FlashAttention", follow-up on why the backward pass recomputes instead of
+// storing P). The products are the ones of the standard backward
+// (zerotofrontier "Efficient attention: memory-bound", section "Real code
+// moves even more"): dV = P^T dO, dP = dO V^T, dS from P and dP, dQ and dK
+// from dS, with the softmax Jacobian dS_ij = P_ij (dP_ij - D_i) and
+// D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic.
+//
+// With dropout (the DROP instantiations) both kernels regenerate the
+// forward's keep mask from the same Philox contract: dV = (P Z)^T dO / kappa,
+// dP is replaced by (dO V^T) Z / kappa, and D_i = rowsum(dO * O) still equals
+// sum_j P_ij dP_ij because O already carries the dropout.
+//
+// Two kernels, no atomics (the result is deterministic), dq first:
+//   dq    one workgroup per 32 query rows per wave (8 waves at d = 64, 4 at
+//         d = 128), laid out like the forward
+//         (S^T = K Q^T, one query per lane): dQ^T = K^T dS^T with K^T from
+//         transposed LDS reads. Its prologue also forms each row's
+//         D_i = rowsum(dO * O) and LSE * log2(e) and stores them for dkdv
+//         (two planes: LSE * log2(e) of every row, then -D).
+//   dkdv  one workgroup per 32 keys per wave of a KV head (K and V
+//         fragments held in registers); it walks every query tile of every
+//         query head of the group. S = Q K^T puts one key per lane, so P and
+//         dS feed dV^T = dO^T P and dK^T = Q^T dS straight from the
+//         accumulators; dO^T and Q^T come from ds_read_b64_tr_b16.
+#pragma once
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+// ----------------------------------------------------------------- dk dv
+
+namespace {
+
+// 64-row query tiles in two LDS stages; d = 64: 8 waves of 32 keys with the
+// small-GEMM interleave hint (iglp 0) ordering the LDS reads among the MFMAs;
+// d = 128: 4 waves (the dK/dV accumulators need up to 512 registers per
+// wave; 8 waves spill) and no hint. Both measured fastest on MI355X.
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = 64, int NSTAGE_ = 2, int IGLP_ = (D == 64 ? 0 : -1),
+          int OCC_ = 1>
+struct DkdvCfg {
+  static constexpr int NW = NW_;                     // waves per workgroup
+  static constexpr int OCC = OCC_;                   // workgroups per CU the register budget allows
+  static constexpr int IGLP = IGLP_;                 // compiler interleave strategy for the body (-1: none)
+  static constexpr int NT = 64 * NW;
+  static constexpr int BK = 32 * NW;                 // keys per workgroup (32 per wave)
+  static constexpr int BQ = BQ_;                     // query rows per tile
+  static constexpr int QB = BQ / 32;                 // 32-row blocks per tile
+  static constexpr int ROWB = 2 * D;                 // LDS bytes per row (swizzled, unpadded)
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int QTILE = BQ * ROWB;            // one Q (or dO) tile
+  // row statistics: the lse2 plane, then the -D plane, each in whole 256-byte wave loads
+  static constexpr int SLOT = (BQ * 4 + 255) / 256 * 256;
+  static constexpr int STATS = 2 * SLOT;
+  static constexpr int STAGE = 2 * QTILE + STATS;
+  static constexpr int NSTAGE = NSTAGE_;
+  static constexpr int TILE_DMA = 2 * BQ * CH / 64;  // 128-bit wave loads per tile (Q and dO)
+  static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
+  static constexpr int STAT_DMA = STATS / 256;       // 32-bit wave loads of the statistics
+  static constexpr int VM_PER_TILE = DMA_PER_WAVE + STAT_DMA;
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
+};
+
+}  // namespace
+
+// One workgroup per BK keys of one KV head; each wave owns 32 keys, with its
+// K and V rows held as MFMA B operands. The workgroup walks every query tile
+// (BQ rows) of every query head of the group that can see one of its keys:
+//   S = Q K^T, dP = dO V^T        (A operands: Q and dO rows from LDS)
+//   P = 2^(S c - lse2), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS  (A operands: transposed LDS reads)
+// S puts one key per lane, so P and dS feed the second pair of products
+// straight from the accumulator registers. Q, dO and the row statistics reach
+// LDS through direct-to-LDS loads into a ring of C::NSTAGE tiles (the next
+// tile loads while one is consumed; at d = 64 two stages measured fastest);
+// tiles are stored unpadded with an XOR swizzle.
+template <int D, bool CAUSAL, class C = DkdvCfg<D>, bool WIN = false, bool DROP = false>
+__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+  static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
+  static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
+  constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
+  // dropout: a wave-private 32 x 32 byte tile turns row-major Philox bytes into key columns
+  constexpr int ZTILE = 32 * 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE + (DROP ? C::NW * ZTILE : 0)];
+  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+
+  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = (int)(t % (uint32_t)n_ktiles);   // causal: small kt has the most work
+  const int bhk = (int)(t / (uint32_t)n_ktiles);
+  const int b = bhk / a.Hkv, hk = bhk - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + wave * 32;                 // first key of this wave
+  const int key = kw0 + col;                      // this lane's key
+  const int shift = a.Tk - a.Tq;
+  const size_t kvoff = (size_t)bhk * a.Tk * D;
+
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+    const uint32_t base = key < a.Tk ? (uint32_t)(key * D + 8 * half) * 2 : kOutOfRange;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = as_bf16x8(buf_load_b128(krs, base + ks * 32));
+      vf[ks] = as_bf16x8(buf_load_b128(vrs, base + ks * 32));
+    }
+  }
+
+  f32x16 dv_acc[D / 32], dk_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dv_acc[db][r] = 0.f;
+      dk_acc[db][r] = 0.f;
+    }
+
+  // Query tiles that can see any key of this workgroup, for each query head of the group.
+  int qt_begin = 0;
+  if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
+  int n_qt = (a.Tq + BQ - 1) / BQ;
+  if (WIN) {   // rows past the last key's window see none of these keys
+    const int last_row = k0 + C::BK - 1 - shift + a.window - 1;
+    n_qt = last_row < 0 ? 0 : min(n_qt, last_row / BQ + 1);
+  }
+  const int per_head = max(0, n_qt - qt_begin);
+  const int n_iter = per_head * G;
+
+  // This thread's share of the tile loads: physical chunk p of the tile holds
+  // logical chunk p ^ swz(row) of its row.
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_row[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  bool dma_is_do[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int n = wave * C::DMA_PER_WAVE + i;
+    const int m = n % (C::TILE_DMA / 2);
+    dma_is_do[i] = n >= C::TILE_DMA / 2;
+    const int p = 64 * m + lane;
+    const int r = p / CH, pc = p % CH;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+    dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
+  }
+  const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
+
+  // Tile iterator for the loads (two tiles ahead of the compute).
+  int ld_it = 0, ld_h = 0, ld_qi = qt_begin;
+  auto issue = [&](int stage) {
+    FA_LDS uint8_t* st = smem + stage * STAGE;
+    const bool live = ld_it < n_iter;
+    const int q0 = ld_qi * BQ;
+    const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.stats + rows, (uint32_t)a.Tq * 4);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.stats + plane + rows, (uint32_t)a.Tq * 4);
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const bool ok = live && q0 + (int)dma_row[i] < a.Tq;
+      const uint32_t off = ok ? (uint32_t)q0 * D * 2 + dma_off[i] : kOutOfRange;
+      dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], off);
+    }
+#pragma unroll
+    for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
+      constexpr int PER_PLANE = C::STAT_DMA / 2;
+      const int pl = i / PER_PLANE, row = 64 * (i % PER_PLANE) + lane;
+      const bool sok = live && row < BQ && q0 + row < a.Tq;   // other lanes write zeros inside the slot
+      dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE),
+              sok ? (uint32_t)(q0 + row) * 4 : kOutOfRange);
+    }
+    ++ld_it;
+    if (++ld_qi == n_qt) {
+      ld_qi = qt_begin;
+      ++ld_h;
+    }
+  };
+
+  // LDS read offsets (bytes inside a tile).
+  const uint32_t fq = swz<D>(col);
+  const uint32_t q_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
+  const int grp = lane >> 4, gi = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+  const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
+  const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
+  const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
+  const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
+
+  FA_LDS uint8_t* ztile = smem + C::NSTAGE * STAGE + wave * ZTILE;
+
+  auto body = [&](const FA_LDS uint8_t* st, int q0, int head, auto masked) {
+    const FA_LDS uint8_t* qt = st;
+    const FA_LDS uint8_t* gt = st + QTILE;
+    const FA_LDS uint8_t* stt = st + 2 * QTILE;
+    const uint32_t bhq = (uint32_t)(b * a.Hq + hk * G + head);   // flattened query head (dropout stream)
+    // S = Q K^T and dP = dO V^T for BQ queries x 32 keys (one key per lane).
+    // On unmasked tiles without dropout the dP product starts from -D
+    // (accumulator register r of block qb holds row 32 qb + 8 (r / 4) +
+    // 4 half + r % 4, so four -D values of consecutive rows fill registers
+    // 4 g4 .. 4 g4 + 3), and dP - D comes out of the matrix cores; masked
+    // tiles (fewer, and short of registers) and dropout add -D afterwards.
+    constexpr bool FOLD = !DROP && !decltype(masked)::value;
+    f32x16 s[QB], dp[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 dinit{};
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 nd = *(const FA_LDS f32x4*)(stt + C::SLOT + (qb * 32 + 8 * g4 + 4 * half) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dinit[4 * g4 + e] = nd[e];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t off = qb * 32 * ROWB + (q_rd ^ (32 * ks));
+        // the first products start from an inline zero (no register clearing) or from -D
+        s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], ks == 0 ? f32x16{} : s[qb]);
+        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? dinit : dp[qb]);
+      }
+    }
+    // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
+    // Masked tiles: row q0 + 32 qb + 8 g4 + 4 half + e sees this lane's key iff
+    // 0 <= dist < window with dist = (that row + shift - key) = dbase + 32 qb + 8 g4 + e.
+    const int dbase = q0 + 4 * half + shift - key;
+    uint32_t pw[QB][8], dsw[QB][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // Dropout bytes for (row 32 qb + 8 g4 + 4 half + e, this lane's key), in
+      // register order 4 g4 + e. Lane (c, h) draws row 32 qb + c's bytes for
+      // the 16 keys kw0 + 16 h .. +15 (the forward's Philox contract), stores
+      // them row-major in the wave's tile and reads back its own key column.
+      uint32_t zbyte[16];
+      if constexpr (DROP) {
+        const u32x4 w = philox4x32_10((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
+                                      a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+        lds_write_b128(ztile, col * 32 + 16 * half, w);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zbyte[i] = ztile[(8 * (i >> 2) + 4 * half + (i & 3)) * 32 + col];
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rq = qb * 32 + 8 * g4 + 4 * half;
+        const f32x4 l2 = *(const FA_LDS f32x4*)(stt + rq * 4);   // lse2 of rows rq .. rq + 3
+        f32x4 nd{};                                               // their -D, unless folded into dP
+        if constexpr (!FOLD) nd = *(const FA_LDS f32x4*)(stt + C::SLOT + rq * 4);
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
+          if constexpr (decltype(masked)::value) {
+            const int dist = dbase + (qb * 32 + 8 * g4 + e);   // one unsigned compare for the band
+            if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
+          }
+          float dpe = dp[qb][r];   // dP - D when folded, else dP
+          float pv = pe;
+          if constexpr (DROP) {   // dV takes the kept P; dP is dropped and rescaled
+            const bool keep = zbyte[r] < a.drop.t;
+            pv = keep ? pe : 0.f;
+            dpe = keep ? dpe * a.drop.inv_keep : 0.f;
+          }
+          if constexpr (!FOLD) dpe += nd[e];
+          p[e] = pv;
+          ds[e] = pe * dpe;
+        }
+        pw[qb][2 * g4] = pack_bf16x2(p[0], p[1]);
+        pw[qb][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
+        dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
+        dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+      }
+    }
+    // (the hint on the unmasked body only: on the masked one it costs registers)
+    if constexpr (C::IGLP >= 0 && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(C::IGLP);
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 pb = as_bf16x8(u32x4{pw[qb][4 * hs], pw[qb][4 * hs + 1], pw[qb][4 * hs + 2], pw[qb][4 * hs + 3]});
+        const bf16x8 sb = as_bf16x8(u32x4{dsw[qb][4 * hs], dsw[qb][4 * hs + 1], dsw[qb][4 * hs + 2], dsw[qb][4 * hs + 3]});
+        const uint32_t hb = (qb * 32 + hs * 16) * ROWB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2 glo = lds_read_tr(gt, hb + (tr_lo ^ (64 * db)));
+          const u32x2 ghi = lds_read_tr(gt, hb + (tr_hi ^ (64 * db)));
+          dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
+          const u32x2 qlo = lds_read_tr(qt, hb + (tr_lo ^ (64 * db)));
+          const u32x2 qhi = lds_read_tr(qt, hb + (tr_hi ^ (64 * db)));
+          dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+        }
+      }
+  };
+
+  // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
+  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::VM_PER_TILE;
+  if (n_iter > 0) {
+    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st);
+    wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
+  }
+  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = qt_begin, cur_h = 0;
+  for (int it = 0; it < n_iter; ++it) {
+    issue(ld_stage);                      // tile it+NSTAGE-1 (zeros past the end)
+    const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
+    const int q0 = cur_qi * BQ;
+    // some (row, key) pair of this wave is masked (causal limit or window start)
+    if ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0))
+      body(st, q0, cur_h, std::true_type{});
+    else
+      body(st, q0, cur_h, std::false_type{});
+    wait_vm_barrier<AHEAD_VM>();          // tile it+1 has landed; this stage is free
+    cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
+    ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
+    if (++cur_qi == n_qt) {
+      cur_qi = qt_begin;
+      ++cur_h;
+    }
+  }
+  if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
+
+  if (key < a.Tk) {
+    uint16_t* dkp = a.dk + kvoff + (size_t)key * D;
+    uint16_t* dvp = a.dv + kvoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        const f32x16& kk = dk_acc[db];
+        const f32x16& vv = dv_acc[db];
+        *(u32x2*)(dkp + d0) = u32x2{pack_bf16x2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale),
+                                    pack_bf16x2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale)};
+        const float sv = DROP ? a.drop.inv_keep : 1.f;   // dV = (P Z)^T dO * 256 / t
+        *(u32x2*)(dvp + d0) = u32x2{pack_bf16x2(vv[4 * g4] * sv, vv[4 * g4 + 1] * sv),
+                                    pack_bf16x2(vv[4 * g4 + 2] * sv, vv[4 * g4 + 3] * sv)};
+      }
+  }
+}
+
+// -------------------------------------------------------------------- dq
+
+namespace {
+
+// d = 64: 8 waves (two per SIMD at about 128 registers, so two workgroups per
+// CU) and 32-key tiles; d = 128: 4 waves with up to 512 registers each (8
+// waves spill), 64-key tiles and the MFMA/exp interleave hint. Both measured
+// fastest on MI355X.
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = (D == 64 ? 32 : 64), int NSTAGE_ = (D == 64 ? 2 : 3),
+          int IGLP_ = (D == 64 ? -1 : 2), int OCC_ = 1>
+struct DqCfg {
+  static constexpr int NW = NW_;                      // waves per workgroup
+  static constexpr int OCC = OCC_;                    // workgroups per CU the register budget allows
+  static constexpr int IGLP = IGLP_;                  // compiler interleave strategy for the body (-1: none)
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;                  // query rows per workgroup
+  static constexpr int BC = BC_;                      // keys per tile
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CH = D / 8;
+  static constexpr int KTILE = BC * ROWB;             // one K (or V) tile
+  static constexpr int STAGE = 2 * KTILE;
+  static constexpr int NSTAGE = NSTAGE_;
+  static constexpr int TILE_DMA = 2 * BC * CH / 64;   // 128-bit wave loads per tile (K and V)
+  static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
+};
+
+}  // namespace
+
+// One workgroup per BR query rows; each wave owns 32 rows, with its Q and dO
+// rows held as MFMA B operands, and walks the key tiles its rows can see:
+//   S^T = K Q^T, dP^T = V dO^T        (A operands: K and V rows from LDS)
+//   P = 2^(S c - lse2), dS = P (dP - D)
+//   dQ^T += K^T dS^T                   (A operand: transposed reads of K)
+// The layout mirrors the forward kernel: one query per lane, so dS^T feeds
+// the last product from the accumulator registers. K and V arrive through
+// direct-to-LDS loads into a ring of C::NSTAGE tiles, swizzled like the
+// dK/dV kernel's tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
+template <int D, bool CAUSAL, class C = DqCfg<D>, bool WIN = false, bool DROP = false>
+__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
+  static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
+  constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
+  constexpr int KB = BC / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
+  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+
+  // Tile order: (batch, kv head) outermost, then query tile, then the query
+  // heads that share the kv head, so the workgroups that run together on an
+  // XCD read the same K/V tiles at about the same time.
+  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t G = (uint32_t)(a.Hq / a.Hkv), per_grp = (uint32_t)n_qtiles * G;
+  const uint32_t kvg = t / per_grp, r = t - kvg * per_grp;
+  const int qt_lin = (int)(r / G), g = (int)(r - (uint32_t)qt_lin * G);
+  const int qt = CAUSAL ? (n_qtiles - 1 - qt_lin) : qt_lin;
+  const int b = (int)kvg / a.Hkv, hk = (int)kvg - b * a.Hkv;
+  const int h = hk * (int)G + g, bh = b * a.Hq + h;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;                 // first row of this wave
+  const int qrow = qw0 + col;                     // this lane's query row
+  const size_t qoff = (size_t)bh * a.Tq;
+  const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
+  const int shift = a.Tk - a.Tq;
+  int kv_end = a.Tk;
+  if (CAUSAL) kv_end = min(a.Tk, q0 + C::BR + shift);
+  const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  // Q and dO rows of this lane's query (B operands; the lane holds half of
+  // the dims, lane ^ 32 the other half), its lse2 = LSE * log2(e) and
+  // D = sum_c dO_c O_c, which are also stored for the dK/dV kernel. A row
+  // that saw no key (LSE = -inf) gets lse2 = +inf, so every rebuilt
+  // probability is 0.
+  bf16x8 qf[D / 16], gf[D / 16];
+  float lse2, delta;
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + qoff * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.o + qoff * D, (uint32_t)a.Tq * D * 2);
+    const bool live = qrow < a.Tq;
+    const uint32_t base = live ? (uint32_t)(qrow * D + 8 * half) * 2 : kOutOfRange;
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 qw = buf_load_b128(qrs, base + ks * 32);
+      const u32x4 gw = buf_load_b128(grs, base + ks * 32);
+      const u32x4 ow = buf_load_b128(ors, base + ks * 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = fmaf(bf16_lo(gw[e]), bf16_lo(ow[e]), dsum);
+        dsum = fmaf(bf16_hi(gw[e]), bf16_hi(ow[e]), dsum);
+      }
+      qf[ks] = as_bf16x8(qw);
+      gf[ks] = as_bf16x8(gw);
+    }
+    delta = pair_sum32(dsum);
+    // rows past Tq: Q = dO = 0, so dS = 0 whatever lse2 holds
+    const float lse = live ? a.lse[qoff + qrow] : 0.f;
+    lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    if (live && half == 0) {   // two planes: lse2 for every row, then -D
+      a.stats[qoff + qrow] = lse2;
+      a.stats[(size_t)a.B * a.Hq * a.Tq + qoff + qrow] = -delta;
+    }
+  }
+
+  f32x16 dq_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
+
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_row[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  bool dma_is_v[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int n = wave * C::DMA_PER_WAVE + i;
+    const int m = n % (C::TILE_DMA / 2);
+    dma_is_v[i] = n >= C::TILE_DMA / 2;
+    const int p = 64 * m + lane;
+    const int r = p / CH, pc = p % CH;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+    dma_dst[i] = (dma_is_v[i] ? KTILE : 0) + m * 1024;
+  }
+  auto issue = [&](int j, int stage) {
+    FA_LDS uint8_t* st = smem + stage * STAGE;
+    const int k0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const bool ok = j < n_kv && k0 + (int)dma_row[i] < a.Tk;
+      dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], ok ? (uint32_t)k0 * D * 2 + dma_off[i] : kOutOfRange);
+    }
+  };
+
+  const uint32_t fq = swz<D>(col);
+  const uint32_t k_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
+  const int grp = lane >> 4, gi = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+  const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
+  const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
+  const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
+  const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
+  const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
+  const int lo = WIN ? qrow + shift - a.window + 1 : 0;   // window start of this lane's row
+  // tiles before j_begin are invisible to every row of the workgroup
+  const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
+
+  // Dropout: the Philox bytes of this lane's row for the 32-key blocks of the
+  // current tile (the forward's layout and contract); the next tile's are
+  // drawn while the matrix cores run this tile's dQ product.
+  u32x4 zcur[KB];
+  auto drop_bytes = [&](int j, int kb) -> u32x4 {
+    return dropout_bytes_32keys((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+                                a.drop.seed_lo, a.drop.seed_hi, half);
+  };
+
+  // At d = 128 without dropout every dP^T chain starts from a register block
+  // holding -D (one query per lane, so one value), read as the first
+  // product's accumulator input: dP - D comes out of the matrix cores at no
+  // per-tile cost. (d = 64 has no 16 registers to spare at two workgroups per
+  // CU; dropout needs dP itself.)
+  constexpr bool FOLD = D == 128 && !DROP;
+  f32x16 ndelta;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndelta[r] = FOLD ? -delta : 0.f;
+
+  auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) {
+    const FA_LDS uint8_t* kt = st;
+    const FA_LDS uint8_t* vt = st + KTILE;
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
+        s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], ks == 0 ? f32x16{} : s[kb]);
+        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? (FOLD ? ndelta : f32x16{}) : dp[kb]);
+      }
+    }
+    uint32_t dsw[KB][8];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 zb = zcur[kb];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = exp2_fast(fmaf(s[kb][r], a.c, -lse2));
+        float p1 = exp2_fast(fmaf(s[kb][r + 1], a.c, -lse2));
+        if constexpr (decltype(masked)::value) {
+          const int kr = j * BC + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (kr > lim || (WIN && kr < lo)) p0 = 0.f;
+          if (kr + 1 > lim || (WIN && kr + 1 < lo)) p1 = 0.f;
+        }
+        float dp0 = dp[kb][r], dp1 = dp[kb][r + 1];
+        if constexpr (DROP) {   // dP of a dropped entry is 0, of a kept one scaled by 256 / t
+          dp0 = dropout_keep(zb, r, a.drop.t) ? dp0 * a.drop.inv_keep : 0.f;
+          dp1 = dropout_keep(zb, r + 1, a.drop.t) ? dp1 * a.drop.inv_keep : 0.f;
+        }
+        const float dsub = FOLD ? 0.f : delta;   // folded: dp already holds dP - D
+        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp0 - dsub), p1 * (dp1 - dsub));
+      }
+    }
+    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
+    // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 sb = as_bf16x8(u32x4{dsw[kb][4 * hs], dsw[kb][4 * hs + 1], dsw[kb][4 * hs + 2], dsw[kb][4 * hs + 3]});
+        const uint32_t rb = (kb * 32 + hs * 16) * ROWB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2 lo = lds_read_tr(kt, rb + (tr_lo ^ (64 * db)));
+          const u32x2 hi = lds_read_tr(kt, rb + (tr_hi ^ (64 * db)));
+          dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
+        }
+      }
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j + 1, kb);
+    }
+  };
+
+  // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
+  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
+  if constexpr (DROP) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
+  }
+  if (j_begin < n_kv) {
+    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(j_begin + st, st);
+    wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
+  }
+  int cur_stage = 0, ld_stage = C::NSTAGE - 1;
+  for (int j = j_begin; j < n_kv; ++j) {
+    issue(j + C::NSTAGE - 1, ld_stage);
+    const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
+    // some (row, key) pair of this wave is masked (causal limit or window start)
+    if ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1))
+      body(st, j, std::true_type{});
+    else
+      body(st, j, std::false_type{});
+    wait_vm_barrier<AHEAD_VM>();
+    cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
+    ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
+  }
+  if (j_begin < n_kv) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
+
+  if (qrow < a.Tq) {
+    uint16_t* dst = a.dq + (qoff + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        const f32x16& q = dq_acc[db];
+        *(u32x2*)(dst + d0) = u32x2{pack_bf16x2(q[4 * g4] * a.scale, q[4 * g4 + 1] * a.scale),
+                                    pack_bf16x2(q[4 * g4 + 2] * a.scale, q[4 * g4 + 3] * a.scale)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
+static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  // dq first: it also stores the per-row statistics the dK/dV kernel reads
+  const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DqCfg<D>, WIN, DROP>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
+                     a, n_qtiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // masked d = 64 tiles: 32-row query tiles (the 64-row masked body spills at
+  // two waves per SIMD; measured 27% faster on a causal T2048 layer)
+  // causal d = 128 with dropout: 32-row tiles as well (the mask bytes push the
+  // 64-row masked body past 512 registers)
+  using KC = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
+             typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>, DkdvCfg<D>>::type>::type;
+  const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0, stream,
+                     a, n_ktiles);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -96,6 +96,7 @@ hipError_t launch_fwd_fp8(Fp8Args a, int d, bool causal, hipStream_t stream);
 int fwd_fp8_rows_per_workgroup(int d);
 hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_window(BwdArgs a, int d, hipStream_t stream);   // a.window >= 1
 
 // Kernels address one head's rows through 32-bit buffer offsets below 2^31.
 constexpr long long kMaxHeadBytes = 1ll << 31;
