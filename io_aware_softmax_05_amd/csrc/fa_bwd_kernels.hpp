@@ -247,7 +247,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
       // them row-major in the wave's tile and reads back its own key column.
       uint32_t zbyte[16];
       if constexpr (DROP) {
-        const u32x4 w = philox4x32_10((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
+        const u32x4 w = philox4x32_10<false>((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
                                       a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
         lds_write_b128(ztile, col * 32 + 16 * half, w);
 #pragma unroll
@@ -509,7 +509,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   // drawn while the matrix cores run this tile's dQ product.
   u32x4 zcur[KB];
   auto drop_bytes = [&](int j, int kb) -> u32x4 {
-    return dropout_bytes_32keys((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+    // plain XORs here: the bitop3 form costs this kernel a register past the
+    // two-workgroups-per-CU budget at d = 64 (and spills in dK/dV)
+    return dropout_bytes_32keys<false>((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
                                 a.drop.seed_lo, a.drop.seed_hi, half);
   };
 

@@ -145,6 +145,14 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) {
 // high halves with words 1 and 3 and the key; the key is bumped by the two
 // Weyl constants between rounds. The key is the same in every lane, so its
 // schedule stays in scalar registers.
+// a ^ b ^ c in one v_bitop3_b32 (truth table 0x96; gfx950 has no v_xor3).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
+// BITOP3 picks the XOR form: v_bitop3_b32 (fewer instructions) or two
+// v_xor_b32 (fewer live registers in some kernels); the result is the same.
+template <bool BITOP3 = true>
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -155,8 +163,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     }
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = BITOP3 ? xor3((uint32_t)(p1 >> 32), c1, k0) : (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = BITOP3 ? xor3((uint32_t)(p0 >> 32), c3, k1) : (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -173,9 +181,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // = bits 8 (n mod 4) .. +7 of word n / 4). Lane l computes the call for
 // group k0 / 16 + l / 32 and swaps the words its partner lane l ^ 32 needs:
 // word q of the result holds the bytes of keys 8 q + 4 (l / 32) + 0..3.
+template <bool BITOP3 = true>
 __device__ __forceinline__ u32x4 dropout_bytes_32keys(uint32_t key0, uint32_t row, uint32_t head, uint32_t offset,
                                                       uint32_t seed_lo, uint32_t seed_hi, int half) {
-  const u32x4 w = philox4x32_10(key0 / 16 + (uint32_t)half, row, head, offset, seed_lo, seed_hi);
+  const u32x4 w = philox4x32_10<BITOP3>(key0 / 16 + (uint32_t)half, row, head, offset, seed_lo, seed_hi);
   // v_permlane32_swap(x, y): lanes 0-31 get {x[l], x[l + 32]}, lanes 32-63 {y[l - 32], y[l]}
   const auto s01 = __builtin_amdgcn_permlane32_swap(w[0], w[1], false, false);
   const auto s23 = __builtin_amdgcn_permlane32_swap(w[2], w[3], false, false);
