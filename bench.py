@@ -534,7 +534,7 @@ def main():
     if args.record_traffic:
         return record_traffic(args.record_traffic)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only (no multi-GPU path); --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (there is no multi-GPU path); --gpus must be 1"}))
         return 2
 
     import torch
