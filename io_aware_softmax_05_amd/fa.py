@@ -220,37 +220,100 @@ def fa_decode_splitkv_window(q, k_cache, v_cache, seq_lens, o, lse, workspace, w
 
 
 # ------------------------------------------------ tensor-level conveniences
+#
+# The kernels index every tensor by the sizes passed with q, so a tensor of
+# another shape would be read or written past its end. The helpers therefore
+# check every tensor's dtype, rank, contiguity and shape against q, and that
+# all of them sit on one GPU, before anything reaches the library.
 
-def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
-    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor with {ndim} dims, "
-                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+def _need(t, dtype, ndim: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
+        got = f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}" if isinstance(t, torch.Tensor) else type(t)
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor with {ndim} dims, got {got}")
+
+
+def _need_shape(t: torch.Tensor, shape, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _one_gpu(**tensors) -> torch.device:
+    devs = {t.device for t in tensors.values() if t is not None}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on one device, got " +
+                         ", ".join(f"{n}: {t.device}" for n, t in tensors.items() if t is not None))
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+    return dev
+
+
+def _check_forward_args(q, k, v) -> None:
+    dt = q.dtype if isinstance(q, torch.Tensor) else None
+    if dt not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"q must be bfloat16 or float32, got {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, dt, 4, name)
+    B, Hq, _, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    _need_shape(k, (B, Hkv, Tk, d), "k")
+    _need_shape(v, k.shape, "v")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError(f"the number of query heads ({Hq}) must be a multiple of the KV heads ({Hkv})")
+    _one_gpu(q=q, k=k, v=v)
+
+
+def _check_backward_args(q, k, v, o, dout, lse) -> None:
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, torch.bfloat16, 4, name)
+    _need(lse, torch.float32, 3, "lse")
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    _need_shape(k, (B, Hkv, Tk, d), "k")
+    _need_shape(v, k.shape, "v")
+    _need_shape(o, q.shape, "o")
+    _need_shape(dout, q.shape, "dout")
+    _need_shape(lse, (B, Hq, Tq), "lse")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError(f"the number of query heads ({Hq}) must be a multiple of the KV heads ({Hkv})")
+    _one_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse)
+
+
+def _check_decode_args(q, k_cache, v_cache, seq_lens, workspace=None, ws_bytes: int = 0) -> None:
+    _need(q, torch.bfloat16, 3, "q")
+    _need(k_cache, torch.bfloat16, 4, "k_cache")
+    _need(v_cache, torch.bfloat16, 4, "v_cache")
+    _need(seq_lens, torch.int32, 1, "seq_lens")
+    B, Hq, d = q.shape
+    Hkv, Tk_max = k_cache.shape[1], k_cache.shape[2]
+    _need_shape(k_cache, (B, Hkv, Tk_max, d), "k_cache")
+    _need_shape(v_cache, k_cache.shape, "v_cache")
+    _need_shape(seq_lens, (B,), "seq_lens")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError(f"the number of query heads ({Hq}) must be a multiple of the KV heads ({Hkv})")
+    if workspace is not None:
+        _need(workspace, torch.uint8, 1, "workspace")
+        if workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {ws_bytes} are needed")
+    _one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, workspace=workspace)
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, with_lse: bool = True, stream=None):
     """O (and LSE) for q [B,Hq,Tq,d], k and v [B,Hkv,Tk,d]; bf16 or fp32."""
-    dt = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, dt, 4, name)
+    _check_forward_args(q, k, v)
     B, Hq, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("k and v must both be [B,Hkv,Tk,d] matching q")
     scale = d ** -0.5 if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if with_lse else None
-    fn = fa_fwd if dt == torch.bfloat16 else fa_fwd_f32 if dt == torch.float32 else None
-    if fn is None:
-        raise ValueError(f"unsupported dtype {dt}")
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
     fn(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, stream)
     return o, lse
 
 
 def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None):
     """dQ, dK, dV (bf16) by recomputation from the saved LSE."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _need(t, torch.bfloat16, 4, name)
-    _need(lse, torch.float32, 3, "lse")
+    _check_backward_args(q, k, v, o, dout, lse)
     B, Hq, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     scale = d ** -0.5 if scale is None else scale
@@ -264,16 +327,14 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
 def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, chunk: int = 0, workspace=None,
            stream=None):
     """O [B,Hq,d] and LSE [B,Hq] for one query token per head."""
-    _need(q, torch.bfloat16, 3, "q")
-    _need(k_cache, torch.bfloat16, 4, "k_cache")
-    _need(v_cache, torch.bfloat16, 4, "v_cache")
-    _need(seq_lens, torch.int32, 1, "seq_lens")
+    _check_decode_args(q, k_cache, v_cache, seq_lens)
     B, Hq, d = q.shape
     Hkv, Tk_max = k_cache.shape[1], k_cache.shape[2]
     scale = d ** -0.5 if scale is None else scale
     ws_bytes = fa_decode_workspace_size(B, Hq, Tk_max, d)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check_decode_args(q, k_cache, v_cache, seq_lens, workspace, ws_bytes)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     fa_decode_splitkv(q, k_cache, v_cache, seq_lens, o, lse, workspace, workspace.numel(), B, Hq, Hkv, Tk_max, d,
