@@ -79,3 +79,50 @@ def attention_case(seed, B, Hq, Hkv, Tq, Tk, d, dtype="bf16", with_dout=False, q
     to_dev = dev_bf16 if dtype == "bf16" else dev_f32
     dev = {n: to_dev(a) for n, a in x.items()}
     return host_vals, dev
+
+
+def causal_dkdv_keys_by_row_ranges(raw, scale, hk, keys, row_range=4096, workers=None):
+    """Oracle dK, dV of `keys` for KV head hk of a causal problem with
+    Tq == Tk, as a sum over the query heads of the group and over ranges of
+    query rows (raw: bf16 bit arrays q, k, v, do with batch 1).
+
+    A row range [r0, r1) only sees keys below r1, so its share of a key's
+    gradient is the oracle's dK/dV of that key for the sub-problem of those
+    rows against keys [0, r1): Tq = r1 - r0 and Tk = r1 put the causal
+    diagonal at key r0 + i for local row i, which is the full problem's rule.
+    The shares are independent and run in a thread pool (numpy releases the
+    interpreter lock inside its array operations)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention_ref as ref
+
+    Hq, Tq = raw["q"].shape[1], raw["q"].shape[2]
+    Hkv, d = raw["k"].shape[1], raw["k"].shape[3]
+    assert raw["k"].shape[2] == Tq and raw["q"].shape[0] == 1
+    g = Hq // Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    k = inputs.widen(raw["k"][:, hk:hk + 1])
+    v = inputs.widen(raw["v"][:, hk:hk + 1])
+
+    def share(h, r0, r1):
+        q = inputs.widen(raw["q"][:, h:h + 1, r0:r1])
+        do = inputs.widen(raw["do"][:, h:h + 1, r0:r1])
+        sel = keys < r1
+        if not sel.any():
+            return sel, 0.0, 0.0
+        dk, dv = ref.attention_bwd_dkdv_keys(q, k[:, :, :r1], v[:, :, :r1], do, scale, True, 0, 0, keys[sel])
+        return sel, dk, dv
+
+    jobs = [(h, r0, min(Tq, r0 + row_range)) for h in range(hk * g, (hk + 1) * g) for r0 in range(0, Tq, row_range)]
+    jobs.sort(key=lambda j: -j[2])   # longest first
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    n = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+        for sel, a, b in ex.map(lambda j: share(*j), jobs):
+            dk[sel] += a
+            dv[sel] += b
+    return dk, dv

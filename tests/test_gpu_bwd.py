@@ -136,10 +136,17 @@ def test_full_size_gpt2_medium_backward():
         gu.check_bf16(f"dV[{b},{h}]", gu.host(dv[b:b + 1, h:h + 1]), dv_r)
 
 
+# Early keys of a causal 32k KV head: each sums contributions of the 4 query
+# heads of its group times up to 32768 rows, the longest accumulations of the
+# dK/dV kernel's query-tile walk.
+EARLY_KEYS = np.array([0, 1, 31, 32, 63, 64, 127, 128, 4095, 16384])
+
+
 @pytest.mark.slow
 def test_full_size_causal_gqa_32k_backward():
-    """B1 Hq32 Hkv8 T32768 d128 causal: sampled dQ rows, dK/dV of the last keys
-    of two KV heads (seen by few rows, so the oracle can afford them), and two
+    """B1 Hq32 Hkv8 T32768 d128 causal: sampled dQ rows; dK/dV element by
+    element for the early keys of KV heads 0 and 7 (the longest sums: 4 heads
+    times up to 32768 rows) and for the last 200 keys of both; and two
     identities over every key: sum_j dV_j = sum of the group's dO rows, and
     sum_j dK_j = 0."""
     w = inputs.WORKLOADS[4]
@@ -163,6 +170,9 @@ def test_full_size_causal_gqa_32k_backward():
         dk_r, dv_r = ref.attention_bwd_dkdv_keys(q, k, v, do, w.scale, True, 0, 0, keys)
         gu.check_bf16(f"dK last keys kv {hk}", gu.host(dk[0, hk, keys]), dk_r)
         gu.check_bf16(f"dV last keys kv {hk}", gu.host(dv[0, hk, keys]), dv_r)
+        dk_r, dv_r = gu.causal_dkdv_keys_by_row_ranges(raw, w.scale, hk, EARLY_KEYS)
+        gu.check_bf16(f"dK early keys kv {hk}", gu.host(dk[0, hk, EARLY_KEYS]), dk_r)
+        gu.check_bf16(f"dV early keys kv {hk}", gu.host(dv[0, hk, EARLY_KEYS]), dv_r)
     # identities over all keys, every KV head
     dvs = gu.host(dv).sum(axis=2)                       # [1, Hkv, d]
     want = inputs.widen(raw["do"]).reshape(1, w.Hkv, g, w.Tq, w.d).sum(axis=(2, 3))
