@@ -95,9 +95,13 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
 
 /*
  * Forward pass with fp32 inputs and outputs (same parameter list and layout
- * as fa_fwd, every tensor fp32). Scores, probabilities and accumulators stay
- * in fp32 throughout: this is the accuracy reference path for small problems
- * and the pages' worked rows, not a throughput path. Same errors as fa_fwd.
+ * as fa_fwd, every tensor fp32). It computes the same tiled recurrence as
+ * fa_fwd (kgptalkie "Flash Attention: Why Memory Traffic, Not Compute, Is the
+ * Bottleneck", section "Carry the Actual Values Through Both Tiles"; aimlrounds
+ * "FlashAttention", section "Softmax without seeing the whole row", whose
+ * worked rows are fp32-exact), but scores, probabilities and accumulators stay
+ * in fp32 throughout: this is the accuracy path for small problems and those
+ * worked rows, not a throughput path. Same errors as fa_fwd.
  */
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal,
@@ -119,6 +123,12 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
  * probabilities (times 2^5, at most 2^8) are rounded to e4m3 before the PV
  * product, the running sum uses them unrounded, so O carries a relative error
  * of up to 2^-4 per probability, LSE only the score rounding.
+ * Every q_scale, k_scale and v_scale entry must be finite and > 0: the kernel
+ * takes the row maximum of the raw byte products and multiplies it by the
+ * positive factor scale * log2(e) * q_scale * k_scale, which is the maximum of
+ * the scaled scores only for a positive factor. The factors sit in device
+ * memory, so the host cannot check them: a zero, negative or NaN factor gives
+ * unspecified (possibly non-finite) o and lse, and no error is reported.
  * Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for NULL vt/q_scale/k_scale/
  * v_scale and for Tk not a multiple of 16 (the V^T rows are read in 16-byte
  * chunks); every pointer must be 16-byte aligned except the scale arrays
@@ -223,8 +233,14 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 /*
  * Workspace bytes fa_decode_splitkv needs for KV caches of up to Tk_max
  * positions: per (batch, query head, split) one partial state (m, l, u[d])
- * in fp32, for the largest split count the library may choose. Linear in
- * Tk_max. Returns 0 for non-positive sizes.
+ * in fp32, for the largest split count the library may choose (64-key
+ * splits). Each split is one tile-sized piece of the row whose running
+ * maximum, sum and weighted sum are later merged with the rescale rule
+ * (kgptalkie "Flash Attention: Why Memory Traffic, Not Compute, Is the
+ * Bottleneck", section "Softmax Looks Like an Obstacle"; aimlrounds
+ * "FlashAttention", note under the "FlashAttention 1, 2, 3" table on
+ * splitting the cache). Linear in Tk_max, never quadratic. Returns 0 for
+ * non-positive sizes.
  */
 size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d);
 

@@ -147,3 +147,26 @@ def test_fp8_forward_full_size_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(T - 64, T),
                                      np.random.Generator(np.random.PCG64(9)).integers(0, T, 128)]))
     _check(x, o, lse, d ** -0.5, True, rows=rows, heads=[(0, 0), (0, 13), (0, 31)])
+
+
+def test_fp8_tiny_positive_factors():
+    # the factors must be finite and > 0; a tiny one is inside that range:
+    # q factor 2^-60 on head 0 and k factor 2^-60 on KV head 1 leave every
+    # score of those heads at about 0, so their rows average V (the oracle's
+    # closed form); v factor 2^-100 on KV head 0 scales its heads' outputs
+    # down by that much, still finite in bf16
+    print("[fp8 tiny factors]", flush=True)
+    x = inputs.draw_fp8_attention_inputs(321, 1, 4, 2, 192, 192, 128)
+    x["q_scale"] = x["q_scale"].copy()
+    x["k_scale"] = x["k_scale"].copy()
+    x["v_scale"] = x["v_scale"].copy()
+    x["q_scale"][0, 0] *= np.float32(2.0 ** -60)
+    x["k_scale"][0, 1] *= np.float32(2.0 ** -60)
+    for causal in (False, True):
+        o, lse = _run(x, 128 ** -0.5, causal)
+        _check(x, o, lse, 128 ** -0.5, causal)
+    x["v_scale"][0, 0] *= np.float32(2.0 ** -100)
+    o, lse = _run(x, 128 ** -0.5, True)
+    og = gu.host(o)
+    assert np.all(np.isfinite(og)) and np.any(og[0, :2] != 0)
+    assert float(np.max(np.abs(og[0, :2]))) < 2.0 ** -90

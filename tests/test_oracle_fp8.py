@@ -147,3 +147,20 @@ def test_draw_recipe_shapes_and_determinism():
     for key in a:
         assert np.array_equal(a[key], b[key])
     assert not np.isnan(ref.e4m3_to_f64(a["q8"])).any()
+
+
+def test_tiny_positive_q_factor_averages_the_values():
+    # the documented range of the factors is finite and > 0; at the small end
+    # (q factor 2^-60) every score is below 2^-40, so each row's softmax is
+    # uniform to within that and O is the mean of the dequantised values over
+    # the visible keys (LSE = ln of their count)
+    d = inputs.draw_fp8_attention_inputs(11, 1, 2, 1, 40, 40, 64)
+    qs = d["q_scale"] * np.float32(2.0 ** -60)
+    vv = ref.e4m3_to_f64(d["vt8"][0, 0]).T * float(d["v_scale"][0, 0])
+    for causal in (False, True):
+        o, lse = ref.attention_fwd_fp8(d["q8"], d["k8"], d["vt8"], qs, d["k_scale"], d["v_scale"], 0.125, causal)
+        for i in range(40):
+            n = i + 1 if causal else 40
+            want = vv[:n].mean(axis=0)
+            assert np.allclose(o[0, 0, i], want, rtol=1e-9, atol=1e-12)
+            assert math.isclose(lse[0, 1, i], math.log(n), rel_tol=1e-9, abs_tol=1e-9)
