@@ -22,6 +22,7 @@
 //   the same rescale rule (m* = max m_s; l = sum 2^(m_s - m*) l_s; same for
 //   u), then writes O = u / l and the log-sum-exp.
 #include <algorithm>
+#include <atomic>
 
 #include "fa_common.hpp"
 #include "fa_internal.h"
@@ -356,6 +357,31 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (a.lse != nullptr && lane == 0) a.lse[bh] = (mstar + log2_fast(l_tot)) * kLn2;
 }
 
+// Devices whose per-device facts are cached (compute-unit count, address of
+// the fixed scratch); a device index at or beyond it is looked up every call
+// (compute units) or refused (scratch).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, looked up once per device: the
+// persistent split grid is sized from it.
+static hipError_t current_cu_count(int* n_cu) {
+  static std::atomic<int> cached[kMaxDevices];   // 0: not looked up yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cacheable = dev >= 0 && dev < kMaxDevices;
+  if (cacheable) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *n_cu = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && cacheable && *n_cu > 0) cached[dev].store(*n_cu, std::memory_order_relaxed);
+  return e;
+}
+
 // Split plus merge with an NSTAGE ring and WG_PER_CU resident workgroups per
 // compute unit (the grid never exceeds the item count's upper bound).
 template <int D, int NSTAGE, int WG_PER_CU>
@@ -363,10 +389,8 @@ hipError_t launch_decode_cfg(const DecodeArgs& a, hipStream_t stream) {
   using C = DecCfg<D, NSTAGE>;
   const int G = a.Hq / a.Hkv;
   const int n_rowgroups = (G + 15) / 16;
-  int dev = 0, n_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  int n_cu = 0;
+  hipError_t e = current_cu_count(&n_cu);
   if (e != hipSuccess) return e;
   const long long slots = (long long)a.B * a.Hkv * n_rowgroups * a.n_splits;
   const long long grid = std::min<long long>(slots, (long long)std::max(1, n_cu) * WG_PER_CU);
