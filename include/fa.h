@@ -286,6 +286,36 @@ int fa_decode_splitkv_window(const void* q, const void* k_cache, const void* v_c
                              int B, int Hq, int Hkv, int Tk_max, int d, float scale, int window, int chunk,
                              hipStream_t stream);
 
+/* Bytes of the fixed device scratch behind fa_decode_splitkv_noalloc (16 MiB). */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * Split-KV decoding that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Parameters, layouts,
+ * results and errors are those of fa_decode_splitkv without the workspace
+ * arguments, and for the same chunk the output is bitwise identical to
+ * fa_decode_splitkv's (the same kernels run).
+ *   - The partial states live in a fixed device scratch of
+ *     FA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ *     runs on until the process ends. A call uses
+ *     2 * r(4 n) + r(4 d n) bytes of it, with n = B * Hq * ceil(Tk_max / chunk)
+ *     (chunk 0 means 1024) and r() rounding up to a multiple of 256; a call
+ *     that needs more returns FA_ERR_WORKSPACE and launches nothing. (B = 16,
+ *     Hq = 32, Tk_max = 32768, d = 128 needs 8.5 MB at the automatic chunk.)
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's partial states (no part of it has to start at zero). Calls that
+ *     overlap in time on one GPU (on different streams, or from different
+ *     host threads) race on it and give wrong results: serialise them, e.g.
+ *     on one stream.
+ *   - stream must belong to the current device (FA_ERR_INVALID_ARG
+ *     otherwise). FA_ERR_HIP if the scratch's address cannot be looked up.
+ */
+int fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seq_lens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

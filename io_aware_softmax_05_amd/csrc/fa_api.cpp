@@ -8,6 +8,8 @@
 
 #include "fa_internal.h"
 
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_SCRATCH_BYTES, "one scratch size");
+
 namespace {
 
 constexpr int kMaxGrid = 65535;
@@ -228,18 +230,27 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   1, window, stream);
 }
 
-size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d) {
-  if (B <= 0 || Hq <= 0 || Tk_max <= 0 || d <= 0) return 0;
-  const size_t splits = ((size_t)Tk_max + fa::kDecodeMinChunk - 1) / fa::kDecodeMinChunk;
-  const size_t per = (size_t)B * Hq * splits;
+
+// Bytes of the partial states for `per` (batch, query head, split) entries:
+// planes m and l, then u[d], each plane starting on a 256-byte boundary.
+static size_t decode_partials_bytes(size_t per, int d) {
   return round256(per * sizeof(float)) * 2 + round256(per * d * sizeof(float));
 }
 
+size_t fa_decode_workspace_size(int B, int Hq, int Tk_max, int d) {
+  if (B <= 0 || Hq <= 0 || Tk_max <= 0 || d <= 0) return 0;
+  const size_t splits = ((size_t)Tk_max + fa::kDecodeMinChunk - 1) / fa::kDecodeMinChunk;
+  return decode_partials_bytes((size_t)B * Hq * splits, d);
+}
+
+// The caller's workspace (sized for the largest split count the library may
+// choose) or, with workspace == nullptr and fixed_scratch set, the library's
+// fixed device scratch laid out for this call's split count.
 static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        const int* seq_lens, void* o, float* lse,
                        void* workspace, size_t ws_bytes,
                        int B, int Hq, int Hkv, int Tk_max, int d, float scale, int window, int chunk,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool fixed_scratch = false) {
   if (!q || !k_cache || !v_cache || !seq_lens || !o) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, 1, Tk_max, d, scale);
   if (st != FA_OK) return st;
@@ -253,9 +264,26 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   const int n_splits = (Tk_max + chunk - 1) / chunk;
   const int G = Hq / Hkv;
   if (B > kMaxGrid || (int64_t)Hkv * ((G + 15) / 16) > kMaxGrid) return FA_ERR_INVALID_ARG;
-  if (!workspace || !aligned16(workspace) || ws_bytes < fa_decode_workspace_size(B, Hq, Tk_max, d))
-    return FA_ERR_WORKSPACE;
-  const size_t per_full = (size_t)B * Hq * (((size_t)Tk_max + fa::kDecodeMinChunk - 1) / fa::kDecodeMinChunk);
+  size_t per = 0;   // partial-state entries between the planes
+  char* ws = nullptr;
+  if (fixed_scratch) {
+    per = (size_t)B * Hq * n_splits;
+    if (decode_partials_bytes(per, d) > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+    // the scratch address is per device: the stream must run on the current one
+    if (stream != nullptr) {
+      int cur = 0, sdev = 0;
+      if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+      if (cur != sdev) return FA_ERR_INVALID_ARG;
+    }
+    void* p = nullptr;
+    if (fa::decode_scratch(&p) != hipSuccess) return FA_ERR_HIP;
+    ws = static_cast<char*>(p);
+  } else {
+    if (!workspace || !aligned16(workspace) || ws_bytes < fa_decode_workspace_size(B, Hq, Tk_max, d))
+      return FA_ERR_WORKSPACE;
+    per = (size_t)B * Hq * (((size_t)Tk_max + fa::kDecodeMinChunk - 1) / fa::kDecodeMinChunk);
+    ws = static_cast<char*>(workspace);
+  }
   fa::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_cache);
@@ -263,10 +291,9 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.seq_lens = seq_lens;
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
-  char* ws = static_cast<char*>(workspace);
   a.part_m = reinterpret_cast<float*>(ws);
-  a.part_l = reinterpret_cast<float*>(ws + round256(per_full * sizeof(float)));
-  a.part_u = reinterpret_cast<float*>(ws + 2 * round256(per_full * sizeof(float)));
+  a.part_l = reinterpret_cast<float*>(ws + round256(per * sizeof(float)));
+  a.part_u = reinterpret_cast<float*>(ws + 2 * round256(per * sizeof(float)));
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tk_max = Tk_max;
   a.chunk = chunk;
   a.n_splits = n_splits;
@@ -292,6 +319,14 @@ int fa_decode_splitkv_window(const void* q, const void* k_cache, const void* v_c
   if (window < 1) return FA_ERR_INVALID_ARG;
   return decode_impl(q, k_cache, v_cache, seq_lens, o, lse, workspace, ws_bytes, B, Hq, Hkv, Tk_max, d, scale,
                      window, chunk, stream);
+}
+
+int fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seq_lens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Tk_max, int d, float scale, int chunk,
+                              hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, o, lse, nullptr, 0, B, Hq, Hkv, Tk_max, d, scale, 0, chunk,
+                     stream, true);
 }
 
 }  // extern "C"

@@ -407,4 +407,31 @@ hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream) {
   return d == 64 ? launch_decode_cfg<64, 3, 4>(a, stream) : launch_decode_cfg<128, 3, 3>(a, stream);
 }
 
+// ------------------------------------------------------------ fixed scratch
+//
+// The partial states of fa_decode_splitkv_noalloc live in this file-scope
+// device array, so that entry point allocates nothing. Every GPU the library
+// runs on holds its own copy, at its own address, until the process ends. In
+// host code the array's name is only a stand-in: its device address is
+// looked up with hipGetSymbolAddress once per device, with that device
+// current, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::atomic<void*> addr[kMaxDevices];   // null: not looked up yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 }  // namespace fa

@@ -105,4 +105,9 @@ constexpr float kLog2eHost = 1.44269504088896340736f;
 constexpr int kDecodeMinChunk = 64;
 constexpr int kDecodeAutoChunk = 1024;
 
+// Size of the fixed device scratch fa_decode_splitkv_noalloc keeps its
+// partial states in, and the lookup of its address on the current device.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

@@ -53,7 +53,10 @@ _SIGNATURES = {
     "fa_decode_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_decode_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
 }
+
+FA_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -217,6 +220,14 @@ def fa_decode_splitkv_window(q, k_cache, v_cache, seq_lens, o, lse, workspace, w
                                                  _ptr(lse), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tk_max,
                                                  d, float(scale), int(window), int(chunk), _stream(stream))
     _check(st, "fa_decode_splitkv_window")
+
+
+def fa_decode_splitkv_noalloc(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, Tk_max, d, scale, chunk=0,
+                              stream=None) -> None:
+    st = load_library().fa_decode_splitkv_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(o),
+                                                  _ptr(lse), B, Hq, Hkv, Tk_max, d, float(scale), int(chunk),
+                                                  _stream(stream))
+    _check(st, "fa_decode_splitkv_noalloc")
 
 
 # ------------------------------------------------ tensor-level conveniences
