@@ -158,8 +158,13 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   }
   const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
 
-  // Tile iterator for the loads (two tiles ahead of the compute).
-  int ld_it = 0, ld_h = 0, ld_qi = qt_begin;
+  // Iteration order: query tiles from the last one down to the first that
+  // sees this workgroup's keys, and for each tile every query head of the
+  // group. The workgroups resident on one XCD hold consecutive key tiles of
+  // one KV head, so they start on the same (tile, head) and walk in step:
+  // each Q/dO tile they read is fetched once into that XCD's L2 instead of
+  // once per workgroup. Tile iterator for the loads (ahead of the compute):
+  int ld_it = 0, ld_h = 0, ld_qi = n_qt - 1;
   auto issue = [&](int stage) {
     FA_LDS uint8_t* st = smem + stage * STAGE;
     const bool live = ld_it < n_iter;
@@ -184,9 +189,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
               sok ? (uint32_t)(q0 + row) * 4 : kOutOfRange);
     }
     ++ld_it;
-    if (++ld_qi == n_qt) {
-      ld_qi = qt_begin;
-      ++ld_h;
+    if (++ld_h == G) {
+      ld_h = 0;
+      if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
     }
   };
 
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st);
     wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
   }
-  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = qt_begin, cur_h = 0;
+  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = n_qt - 1, cur_h = 0;
   for (int it = 0; it < n_iter; ++it) {
     issue(ld_stage);                      // tile it+NSTAGE-1 (zeros past the end)
     const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
@@ -326,9 +331,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     wait_vm_barrier<AHEAD_VM>();          // tile it+1 has landed; this stage is free
     cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
     ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
-    if (++cur_qi == n_qt) {
-      cur_qi = qt_begin;
-      ++cur_h;
+    if (++cur_h == G) {
+      cur_h = 0;
+      --cur_qi;
     }
   }
   if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
