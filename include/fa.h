@@ -182,6 +182,33 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   hipStream_t stream);
 
 /*
+ * fa_fwd and fa_bwd computed with a chosen compiled tiling, for checking that
+ * the result does not depend on the tile shape (aimlrounds "FlashAttention",
+ * section "Softmax without seeing the whole row": the tiled recurrence gives
+ * the same answer for every tile size, up to floating-point rounding).
+ *   tile_shape 0: the tiling fa_fwd and fa_bwd use (the same kernels);
+ *   tile_shape 1: a second tiling of the same kernels --
+ *     forward: 32-key tiles instead of 64, and 128-row query tiles instead
+ *              of 256 at d = 128 (d = 64 keeps its 128-row tiles);
+ *     backward: dQ takes 32-key tiles at d = 128 and 64-key tiles at d = 64
+ *              (the default is the other way round); dK/dV walks 32-row
+ *              query tiles where the default walks 64, and 64 where it
+ *              walks 32 (causal d = 64).
+ * The two tilings round differently (the probabilities are rounded to bf16
+ * relative to a running maximum that moves at tile boundaries), so their
+ * outputs agree to the bf16 tolerance, not bitwise. Parameters, layouts,
+ * workspace and errors are those of fa_fwd and fa_bwd, plus
+ * FA_ERR_INVALID_ARG for a tile_shape other than 0 or 1.
+ */
+int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int tile_shape,
+                 hipStream_t stream);
+int fa_bwd_tiles(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                 int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int tile_shape,
+                 hipStream_t stream);
+
+/*
  * Dropout of the attention probabilities in the fused forward and backward.
  * The zerotofrontier page "Efficient attention: memory-bound" (section "Real
  * code moves even more") lists dropout among the elementwise steps a training

@@ -22,7 +22,7 @@ LIB_NAME = "libfa_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip",
-           "fa_bwd_window.hip"]
+           "fa_bwd_window.hip", "fa_bwd_tiles.hip"]
 
 # Per-source options. fa_bwd.hip: MFMAs in VGPR form (the d = 128 backward's
 # default AGPR form copies every S and dP result back for the vector math;

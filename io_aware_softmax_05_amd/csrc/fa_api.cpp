@@ -71,7 +71,7 @@ int fa_dropout_keep_threshold(float p_drop) {
 
 static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int window,
-                    hipStream_t stream, const fa::DropArgs& drop = fa::DropArgs{}) {
+                    hipStream_t stream, const fa::DropArgs& drop = fa::DropArgs{}, bool alt_tiles = false) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
   if (st != FA_OK) return st;
@@ -89,7 +89,15 @@ static int fwd_impl(const void* q, const void* k, const void* v, void* o, float*
   a.c = scale * fa::kLog2eHost;
   a.window = window;
   a.drop = drop;
+  if (alt_tiles) return to_status(fa::launch_fwd_bf16_alt_tiles(a, d, causal != 0, stream));
   return to_status(fa::launch_fwd_bf16(a, d, causal != 0, stream));
+}
+
+int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int tile_shape,
+                 hipStream_t stream) {
+  if (tile_shape != 0 && tile_shape != 1) return FA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, 0, stream, fa::DropArgs{}, tile_shape == 1);
 }
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -151,7 +159,9 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
-  if ((int64_t)((Tq + 63) / 64) * B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  // one wave per query row, a few rows per workgroup
+  const int rows_per_group = fa::fwd_f32_rows_per_workgroup();
+  if (((int64_t)B * Hq * Tq + rows_per_group - 1) / rows_per_group > INT32_MAX) return FA_ERR_INVALID_ARG;
   fa::FwdF32Args a{};
   a.q = static_cast<const float*>(q);
   a.k = static_cast<const float*>(k);
@@ -171,7 +181,7 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Tq, int d) {
 static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                     int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int window,
-                    hipStream_t stream, const fa::DropArgs& drop = fa::DropArgs{}) {
+                    hipStream_t stream, const fa::DropArgs& drop = fa::DropArgs{}, bool alt_tiles = false) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const int st = check_common(B, Hq, Hkv, Tq, Tk, d, scale);
   if (st != FA_OK) return st;
@@ -199,7 +209,17 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   a.c = scale * fa::kLog2eHost;
   a.window = window;
   a.drop = drop;
+  if (alt_tiles) return to_status(fa::launch_bwd_alt_tiles(a, d, causal != 0, stream));
   return to_status(window > 0 ? fa::launch_bwd_window(a, d, stream) : fa::launch_bwd(a, d, causal != 0, stream));
+}
+
+int fa_bwd_tiles(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                 int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale, int causal, int tile_shape,
+                 hipStream_t stream) {
+  if (tile_shape != 0 && tile_shape != 1) return FA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, causal, 0,
+                  stream, fa::DropArgs{}, tile_shape == 1);
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,

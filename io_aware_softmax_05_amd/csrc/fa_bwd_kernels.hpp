@@ -143,7 +143,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 
   // This thread's share of the tile loads: physical chunk p of the tile holds
   // logical chunk p ^ swz(row) of its row.
-  uint32_t dma_off[C::DMA_PER_WAVE], dma_row[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
   bool dma_is_do[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
@@ -152,7 +152,6 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     dma_is_do[i] = n >= C::TILE_DMA / 2;
     const int p = 64 * m + lane;
     const int r = p / CH, pc = p % CH;
-    dma_row[i] = r;
     dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
     dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
   }
@@ -165,28 +164,26 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   // each Q/dO tile they read is fetched once into that XCD's L2 instead of
   // once per workgroup. Tile iterator for the loads (ahead of the compute):
   int ld_it = 0, ld_h = 0, ld_qi = n_qt - 1;
-  auto issue = [&](int stage) {
-    FA_LDS uint8_t* st = smem + stage * STAGE;
+  // Rows past Tq lie past the end of the buffer ranges and read as zeros, so
+  // only an exhausted iterator needs an out-of-range base.
+  auto issue = [&](auto stage_c) FA_INLINE {
+    FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
     const bool live = ld_it < n_iter;
-    const int q0 = ld_qi * BQ;
     const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.stats + rows, (uint32_t)a.Tq * 4);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.stats + plane + rows, (uint32_t)a.Tq * 4);
+    const uint32_t tbase = live ? (uint32_t)(ld_qi * BQ) * D * 2 : kOutOfRange;
+    const uint32_t sbase = live ? (uint32_t)(ld_qi * BQ) * 4 : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const bool ok = live && q0 + (int)dma_row[i] < a.Tq;
-      const uint32_t off = ok ? (uint32_t)q0 * D * 2 + dma_off[i] : kOutOfRange;
-      dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], off);
-    }
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], tbase + dma_off[i]);
 #pragma unroll
     for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
+      // lanes past BQ rows (BQ < 64) fill unread bytes of the slot
       constexpr int PER_PLANE = C::STAT_DMA / 2;
       const int pl = i / PER_PLANE, row = 64 * (i % PER_PLANE) + lane;
-      const bool sok = live && row < BQ && q0 + row < a.Tq;   // other lanes write zeros inside the slot
-      dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE),
-              sok ? (uint32_t)(q0 + row) * 4 : kOutOfRange);
+      dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE), sbase + (uint32_t)row * 4);
     }
     ++ld_it;
     if (++ld_h == G) {
@@ -207,7 +204,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 
   FA_LDS uint8_t* ztile = smem + C::NSTAGE * STAGE + wave * ZTILE;
 
-  auto body = [&](const FA_LDS uint8_t* st, int q0, int head, auto masked) {
+  auto body = [&](const FA_LDS uint8_t* st, int q0, int head, auto masked) FA_INLINE {
     const FA_LDS uint8_t* qt = st;
     const FA_LDS uint8_t* gt = st + QTILE;
     const FA_LDS uint8_t* stt = st + 2 * QTILE;
@@ -312,30 +309,34 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
       }
   };
 
-  // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
+  // Ring of NSTAGE tiles, NSTAGE - 1 loads ahead of the compute. The loop is
+  // unrolled NSTAGE times, so every stage is a compile-time LDS offset.
   constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::VM_PER_TILE;
   if (n_iter > 0) {
-    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(st);
+    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(st); });
     wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
   }
-  int cur_stage = 0, ld_stage = C::NSTAGE - 1, cur_qi = n_qt - 1, cur_h = 0;
-  for (int it = 0; it < n_iter; ++it) {
-    issue(ld_stage);                      // tile it+NSTAGE-1 (zeros past the end)
-    const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
+  int cur_qi = n_qt - 1, cur_h = 0;
+  auto step = [&](auto stage_c) FA_INLINE {
+    constexpr int CS = decltype(stage_c)::value;
+    issue(std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});   // zeros past the end
+    const FA_LDS uint8_t* st = smem + CS * STAGE;
     const int q0 = cur_qi * BQ;
     // some (row, key) pair of this wave is masked (causal limit or window start)
     if ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0))
       body(st, q0, cur_h, std::true_type{});
     else
       body(st, q0, cur_h, std::false_type{});
-    wait_vm_barrier<AHEAD_VM>();          // tile it+1 has landed; this stage is free
-    cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
-    ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
+    wait_vm_barrier<AHEAD_VM>();          // the next tile has landed; this stage is free
     if (++cur_h == G) {
       cur_h = 0;
       --cur_qi;
     }
-  }
+  };
+  for (int it = 0; it < n_iter; it += C::NSTAGE)
+    static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+      if (it + decltype(s)::value < n_iter) step(s);
+    });
   if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
   if (key < a.Tk) {
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
-  uint32_t dma_off[C::DMA_PER_WAVE], dma_row[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
   bool dma_is_v[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
@@ -482,18 +483,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     dma_is_v[i] = n >= C::TILE_DMA / 2;
     const int p = 64 * m + lane;
     const int r = p / CH, pc = p % CH;
-    dma_row[i] = r;
     dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
     dma_dst[i] = (dma_is_v[i] ? KTILE : 0) + m * 1024;
   }
-  auto issue = [&](int j, int stage) {
-    FA_LDS uint8_t* st = smem + stage * STAGE;
-    const int k0 = j * BC;
+  // Keys past Tk lie past the end of the buffer ranges and read as zeros, so
+  // only a tile past the loop needs an out-of-range base.
+  auto issue = [&](int j, auto stage_c) FA_INLINE {
+    FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
+    const uint32_t tbase = j < n_kv ? (uint32_t)(j * BC) * D * 2 : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const bool ok = j < n_kv && k0 + (int)dma_row[i] < a.Tk;
-      dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], ok ? (uint32_t)k0 * D * 2 + dma_off[i] : kOutOfRange);
-    }
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], tbase + dma_off[i]);
   };
 
   const uint32_t fq = swz<D>(col);
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 #pragma unroll
   for (int r = 0; r < 16; ++r) ndelta[r] = FOLD ? -delta : 0.f;
 
-  auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) {
+  auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) FA_INLINE {
     const FA_LDS uint8_t* kt = st;
     const FA_LDS uint8_t* vt = st + KTILE;
     f32x16 s[KB], dp[KB];
@@ -586,29 +585,32 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     }
   };
 
-  // Ring of NSTAGE tiles: NSTAGE - 1 loads ahead of the compute.
+  // Ring of NSTAGE tiles, NSTAGE - 1 loads ahead of the compute. The loop is
+  // unrolled NSTAGE times, so every stage is a compile-time LDS offset.
   constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
   if constexpr (DROP) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
   }
   if (j_begin < n_kv) {
-    for (int st = 0; st < C::NSTAGE - 1; ++st) issue(j_begin + st, st);
+    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(j_begin + decltype(st)::value, st); });
     wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
   }
-  int cur_stage = 0, ld_stage = C::NSTAGE - 1;
-  for (int j = j_begin; j < n_kv; ++j) {
-    issue(j + C::NSTAGE - 1, ld_stage);
-    const FA_LDS uint8_t* st = smem + cur_stage * STAGE;
+  auto step = [&](int j, auto stage_c) FA_INLINE {
+    constexpr int CS = decltype(stage_c)::value;
+    issue(j + C::NSTAGE - 1, std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});
+    const FA_LDS uint8_t* st = smem + CS * STAGE;
     // some (row, key) pair of this wave is masked (causal limit or window start)
     if ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1))
       body(st, j, std::true_type{});
     else
       body(st, j, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();
-    cur_stage = cur_stage == C::NSTAGE - 1 ? 0 : cur_stage + 1;
-    ld_stage = ld_stage == C::NSTAGE - 1 ? 0 : ld_stage + 1;
-  }
+  };
+  for (int j = j_begin; j < n_kv; j += C::NSTAGE)
+    static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+      if (j + decltype(s)::value < n_kv) step(j + decltype(s)::value, s);
+    });
   if (j_begin < n_kv) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
   if (qrow < a.Tq) {
@@ -627,23 +629,29 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 
 // ---------------------------------------------------------------- launch
 
-template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
+// The default tiling, or (ALT) a second one of the same kernels, offered to
+// check that the result does not depend on the tile shape: dQ takes 64-key
+// tiles where the default takes 32 and 32 where it takes 64, dK/dV walks
+// 32-row query tiles where the default walks 64 and 64 where it walks 32.
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false, bool ALT = false>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  using QC = typename std::conditional<ALT, DqCfg<D, DqCfg<D>::NW, (DqCfg<D>::BC == 32 ? 64 : 32)>, DqCfg<D>>::type;
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
-  const int n_qtiles = (a.Tq + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DqCfg<D>, WIN, DROP>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(DqCfg<D>::NT), 0, stream,
-                     a, n_qtiles);
+  const int n_qtiles = (a.Tq + QC::BR - 1) / QC::BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QC, WIN, DROP>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(QC::NT), 0,
+                     stream, a, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // masked d = 64 tiles: 32-row query tiles (the 64-row masked body spills at
   // two waves per SIMD; measured 27% faster on a causal T2048 layer)
   // causal d = 128 with dropout: 32-row tiles as well (the mask bytes push the
   // 64-row masked body past 512 registers)
-  using KC = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
+  using KD = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
              typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>, DkdvCfg<D>>::type>::type;
+  using KC = typename std::conditional<ALT, DkdvCfg<D, KD::NW, (KD::BQ == 64 ? 32 : 64)>, KD>::type;
   const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0, stream,
-                     a, n_ktiles);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0,
+                     stream, a, n_ktiles);
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -25,6 +27,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define FA_LDS __attribute__((address_space(3)))
+// Lambdas of a kernel's main loop are always inlined (a call would move
+// their captures to scratch memory and make uniform values per-lane).
+#define FA_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -119,6 +124,17 @@ template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// f(std::integral_constant<int, I>{}) for I = B .. E - 1: loops over ring
+// stages whose index must be a compile-time constant (LDS offsets then become
+// instruction immediates instead of per-iteration address arithmetic).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // XOR swizzle of the 16-byte chunks of a row of D bf16 values, for LDS tiles

@@ -54,11 +54,15 @@ namespace fa {
 
 namespace {
 
-template <int D>
+// Default tiling: 8 waves (256 query rows) at d = 128, 4 waves at d = 64,
+// 64-key tiles. FwdAltCfg is a second tiling of the same kernel (32-key tiles,
+// and 128-row query tiles at d = 128), offered to check that the result does
+// not depend on the tile shape.
+template <int D, int NW_ = (D == 128 ? 8 : 4), int BC_ = 64>
 struct FwdCfg {
-  static constexpr int NW = D == 128 ? 8 : 4;   // waves per workgroup
+  static constexpr int NW = NW_;                // waves per workgroup
   static constexpr int BR = 32 * NW;            // query rows per workgroup
-  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int BC = BC_;                // keys per tile
   static constexpr int NT = 64 * NW;            // threads per workgroup
   static constexpr int KPITCH = (D + 8) * 2;    // LDS bytes per K row
   static constexpr int VPITCH = (D + 32) * 2;   // LDS bytes per V row
@@ -69,16 +73,18 @@ struct FwdCfg {
   static_assert(LOADS >= 1 && LOADS * NT == BC * CH, "a tile must split evenly over the workgroup");
 };
 
+template <int D>
+using FwdAltCfg = FwdCfg<D, 4, 32>;
+
 // Stale-maximum allowance (log2 units): probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.f;
 
 }  // namespace
 
-template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
-__global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false, class C = FwdCfg<D>>
+__global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
   static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
-  using C = FwdCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, NT = C::NT, CH = C::CH, LOADS = C::LOADS;
   constexpr int KPITCH = C::KPITCH, VPITCH = C::VPITCH, KTILE = C::KTILE, VTILE = C::VTILE;
   constexpr int KB = BC / 32;
@@ -367,16 +373,23 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 8 / FwdCfg<D>::NW) void fwd_bf16_ker
   }
 }
 
-template <int D, bool CAUSAL, bool WIN = false, bool DROP = false>
+template <int D, bool CAUSAL, bool WIN = false, bool DROP = false, class C = FwdCfg<D>>
 static hipError_t launch_fwd(FwdArgs a, hipStream_t stream) {
-  using C = FwdCfg<D>;
   a.n_qtiles = (a.Tq + C::BR - 1) / C::BR;
   const uint32_t n = (uint32_t)a.n_qtiles * (uint32_t)(a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WIN, DROP>), dim3(n), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WIN, DROP, C>), dim3(n), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
-int fwd_rows_per_workgroup(int d) { return d == 128 ? FwdCfg<128>::BR : FwdCfg<64>::BR; }
+// the smallest query tile of either tiling (grid-size checks use it)
+int fwd_rows_per_workgroup(int d) { return d == 128 ? FwdAltCfg<128>::BR : FwdAltCfg<64>::BR; }
+
+hipError_t launch_fwd_bf16_alt_tiles(FwdArgs a, int d, bool causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_fwd<64, true, false, false, FwdAltCfg<64>>(a, stream)
+                             : launch_fwd<64, false, false, false, FwdAltCfg<64>>(a, stream);
+  return causal ? launch_fwd<128, true, false, false, FwdAltCfg<128>>(a, stream)
+                : launch_fwd<128, false, false, false, FwdAltCfg<128>>(a, stream);
+}
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
   if (a.window > 0) return d == 64 ? launch_fwd<64, true, true>(a, stream) : launch_fwd<128, true, true>(a, stream);

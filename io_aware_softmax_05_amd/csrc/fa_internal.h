@@ -92,11 +92,15 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
 int fwd_rows_per_workgroup(int d);
 hipError_t launch_fwd_f32(FwdF32Args a, int d, bool causal, hipStream_t stream);
+int fwd_f32_rows_per_workgroup();
 hipError_t launch_fwd_fp8(Fp8Args a, int d, bool causal, hipStream_t stream);
 int fwd_fp8_rows_per_workgroup(int d);
 hipError_t launch_decode(DecodeArgs a, int d, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_window(BwdArgs a, int d, hipStream_t stream);   // a.window >= 1
+// The same passes with the second tiling of their kernels (plain and causal masks).
+hipError_t launch_fwd_bf16_alt_tiles(FwdArgs a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_alt_tiles(BwdArgs a, int d, bool causal, hipStream_t stream);
 
 // Kernels address one head's rows through 32-bit buffer offsets below 2^31.
 constexpr long long kMaxHeadBytes = 1ll << 31;

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_tiles": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_bwd_tiles": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_dropout_keep_threshold": (_I, [_F]),
     "fa_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _P]),
     "fa_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -175,6 +177,20 @@ def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq,
                                       _ptr(dk), _ptr(dv), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tq, Tk, d,
                                       float(scale), int(window), _stream(stream))
     _check(st, "fa_bwd_window")
+
+
+def fa_fwd_tiles(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, causal, tile_shape, stream=None) -> None:
+    st = load_library().fa_fwd_tiles(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
+                                     float(scale), int(bool(causal)), int(tile_shape), _stream(stream))
+    _check(st, "fa_fwd_tiles")
+
+
+def fa_bwd_tiles(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, causal,
+                 tile_shape, stream=None) -> None:
+    st = load_library().fa_bwd_tiles(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(workspace), int(ws_bytes), B, Hq, Hkv, Tq, Tk, d,
+                                     float(scale), int(bool(causal)), int(tile_shape), _stream(stream))
+    _check(st, "fa_bwd_tiles")
 
 
 def fa_dropout_keep_threshold(p_drop) -> int:

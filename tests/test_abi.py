@@ -223,3 +223,24 @@ def test_dropout_entry_points_check_like_the_plain_ones():
         == fa.FA_ERR_INVALID_ARG
     assert lib().fa_bwd_dropout(A, A, A, A, A, A, A, A, A, A, 1 << 20, 1, 3, 2, 8, 8, 64, 0.125, 1, 0.1, 1, 0,
                                 None) == fa.FA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ tile shapes
+
+@pytest.mark.parametrize("shape", [-1, 2, 7])
+def test_tile_shape_entry_points_reject_unknown_shapes(shape):
+    L = lib()
+    assert L.fa_fwd_tiles(A, A, A, A, None, 1, 2, 1, 8, 8, 64, 0.125, 1, shape, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_tiles(A, A, A, A, A, A, A, A, A, A, 1 << 20, 1, 2, 1, 8, 8, 64, 0.125, 1, shape,
+                          None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_tile_shape_entry_points_check_like_the_plain_ones():
+    L = lib()
+    for shape in (0, 1):
+        assert L.fa_fwd_tiles(A, A, A, A, None, 1, 2, 1, 8, 8, 48, 0.125, 1, shape, None) == fa.FA_ERR_UNSUPPORTED
+        assert L.fa_fwd_tiles(A, A, A, A, None, 1, 3, 2, 8, 8, 64, 0.125, 1, shape, None) == fa.FA_ERR_INVALID_ARG
+        assert L.fa_bwd_tiles(A, A, A, A, A, A, A, A, A, None, 1 << 20, 1, 2, 1, 8, 8, 64, 0.125, 1, shape,
+                              None) == fa.FA_ERR_WORKSPACE
+        assert L.fa_bwd_tiles(A, A, A, A, A, A, A, A, A, A, 16, 1, 2, 1, 8, 8, 64, 0.125, 1, shape,
+                              None) == fa.FA_ERR_WORKSPACE
