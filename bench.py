@@ -3,23 +3,31 @@
 
     python bench.py [--steps K] [--warmup W]
 
-One step is one pass of the hot path over one batch: fa_fwd then fa_bwd
-(recomputation from the saved LSE) on the GPT-2-medium attention layer
-(B64 H16 T1024 d64, bf16, non-causal, scale 1/8), with Q, K, V, dO already
-resident in HBM. W untimed steps, then K steps timed between two device
-synchronisations; HIP events recorded around every launch, on the stream the
-kernels run on, give per-launch durations.
+The headline step is one pass of the forward hot path (grid plan, Q-tile
+load, K/V streaming, S = scale QK^T on the matrix cores, causal mask, online
+softmax, u += PV, epilogue) over the causal long-context layer: fa_fwd on
+B1 H32 T8192 d128 bf16 (the Llama-3-8B attention shape of zerotofrontier
+"Efficient attention: memory-bound"), scale 1/sqrt(128), inputs drawn with the
+seeded recipe of io_aware_softmax_05_amd/inputs.py (the same values the parity
+tests check) and resident in HBM before timing starts. W untimed steps, then
+exactly K steps timed between two device synchronisations; HIP events
+recorded around every launch, on the stream the kernel runs on, give the
+launch duration behind `roofline`.
 
-After the timed region, in the same run (not part of `value`), under "targets":
-  * the causal long-context forward (B1 H32 T8192 d128) and split-KV decoding
-    (B16 Hq32 Hkv8, lengths U[4096, 32768] from seed 5, d128), each the median
-    of 50 launches after 10 untimed;
-  * the causal 32k GQA layer (B1 Hq32 Hkv8 T32768 d128) fwd and bwd, the
-    sliding-window layer (same, W4096) fwd and bwd, the fp8 causal forward
-    (B1 H32 T8192 d128) and the GPT-2-medium layer with dropout p = 0.1 fwd and
-    bwd; the fp32 single-head forward (B1 H1 T256 d64) as a latency;
-  * the fp64 CPU oracle is timed on a bounded sample of the step's workload.
-Prints one JSON line.
+Before the headline, in the same run, under "targets" (each the median of
+timed launches after untimed ones, seeded inputs unless stated):
+  * the GPT-2-medium layer fwd+bwd (B64 H16 T1024 d64, non-causal);
+  * the causal 32k GQA layer fwd and bwd (B1 Hq32 Hkv8 T32768 d128);
+  * split-KV decoding (B16 Hq32 Hkv8 Tk<=32768 d128, lengths U[4096, 32768]);
+    the seeded cache and a device copy of it are used in turn, so no call
+    finds the previous call's rows in the 256 MiB MALL;
+  * outside the five workloads, with torch-drawn N(0,1) inputs: the
+    sliding-window layer (B1 Hq32 Hkv8 T32768 W4096 d128) fwd and bwd, the
+    fp8 causal forward (B1 H32 T8192 d128) and the GPT-2-medium layer with
+    dropout p = 0.1;
+  * the fp32 single-head forward (B1 H1 T256 d64) as a latency.
+After the headline: the fp64 CPU oracle timed on the host cores
+(`cpu_baseline`), and the GPU clock read while the headline kernel runs.
 
 FLOP convention: 4*d per visible (query, key) pair for the forward (two
 contractions), 2.5x that for the backward (five contractions); a causal
@@ -36,7 +44,8 @@ written by `--record-traffic DIR` from four rocprofv3 counter runs:
 by the ratio of the known copy size to what that counter reads for the plain
 1 GiB device copy. Each unit records a hash of the sources its kernels are
 built from (plus the shared headers); when those change, that unit's traffic is
-reported as null until the counters are taken again.
+reported as null until the counters are taken again. `--record-counters DIR`
+does the same for the instruction and cycle counters of profiles/counters.json.
 """
 from __future__ import annotations
 
@@ -47,7 +56,10 @@ import glob
 import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -58,23 +70,18 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (AMD spec)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak (AMD spec)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak (AMD spec)
+SPEC_SCLK_MHZ = 2400          # MI355X peak engine clock the matrix peak assumes
 
 COPY_BYTES = 1 << 30          # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "io_aware_softmax_05_amd", "csrc")
 
 METRIC = "attention fwd/bwd TFLOPS and % of MI355X bf16 MFMA peak; decode HBM GB/s"
+HEADLINE_UNIT = "fa_fwd causal B1 H32 T8192 d128"
 
-WORKLOADS = {
-    # name: (B, Hq, Hkv, T, d, causal, seed)
-    "gpt2-medium-fwd-bwd": (64, 16, 16, 1024, 64, False, 2),
-    "causal-8k-fwd": (1, 32, 32, 8192, 128, True, 3),
-    "causal-32k-gqa-fwd-bwd": (1, 32, 8, 32768, 128, True, 4),
-}
-DECODE = dict(B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seed=5)
-
-# Launch units whose HBM traffic is recorded: unit -> kernel names (prefix of
-# the demangled name, up to the argument list).
+# Launch units whose HBM traffic (and counters) are recorded: unit -> kernel
+# names (prefix of the demangled name, up to the argument list).
 TRAFFIC_UNITS = {
     "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false, false, false>"],
     "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false, false, false>", "bwd_dkdv_kernel<64, false, false, false>"],
@@ -129,29 +136,38 @@ def unit_source_hash(unit: str) -> str:
     return source_hash(sorted(files))
 
 
-def recorded_traffic(unit: str):
-    """Measured HBM bytes per launch of `unit`, or None (not recorded, or the
-    kernels changed since the counters were taken)."""
+def _fresh_record(path: str, unit: str):
+    """The record of `unit` in a profiles/ JSON file, or None when it is
+    missing or the unit's kernels changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     u = rec.get("units", {}).get(unit)
     if u is None or unit not in TRAFFIC_UNITS or u.get("source_sha256") != unit_source_hash(unit):
         return None
-    return float(u["bytes"])
+    return u
+
+
+def recorded_traffic(unit: str):
+    """Measured HBM bytes per launch of `unit`, or None (not recorded, or the
+    kernels changed since the counters were taken)."""
+    u = _fresh_record(TRAFFIC_FILE, unit)
+    return None if u is None else float(u["bytes"])
+
+
+def recorded_counters(unit: str):
+    """Derived counter figures of `unit` (matrix-core busy fraction, VALU
+    co-execution, clock, ...) from profiles/counters.json, or None."""
+    u = _fresh_record(COUNTERS_FILE, unit)
+    return None if u is None else u.get("derived")
 
 
 # ------------------------------------------------------------------ GPU timing
 
-def _randn_bf16(shape, gen):
-    import torch
-    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-
-
 class Timer:
-    """HIP events around launches on one stream; averages in ms."""
+    """HIP events around launches on one stream; durations in ms."""
 
     def __init__(self, stream):
         self.stream = stream
@@ -165,111 +181,158 @@ class Timer:
         e.record(self.stream)
         self.pairs.append((s, e))
 
+    def times(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
     def mean_ms(self):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+        return float(np.mean(self.times())) if self.pairs else float("nan")
 
     def median_ms(self):
-        return float(np.median([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+        return float(np.median(self.times())) if self.pairs else float("nan")
+
+
+def timed(calls, steps, warmup, stream):
+    """Run `calls` (list of (name, fn)) warmup times untimed, then `steps`
+    times between two device synchronisations, with events around each call.
+    Returns (wall seconds, {name: Timer})."""
+    import torch
+    timers = {n: Timer(stream) for n, _ in calls}
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for n, fn in calls:
+            timers[n].record(fn)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, timers
+
+
+def to_device(raw):
+    """Seeded host arrays (bf16 bit patterns as uint16, or fp32) -> device tensors."""
+    import torch
+    out = {}
+    for n, a in raw.items():
+        if a.dtype == np.uint16:
+            out[n] = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            out[n] = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return out
+
+
+def roofline(bound, work, ms, unit_name, algorithmic_bytes=None, peak_tflops=PEAK_BF16_TFLOPS):
+    """Roofline entry for one launch unit: `work` is FLOP (bound "mfma", against
+    the matrix peak of the unit's dtype) or bytes (bound "hbm") per launch, `ms`
+    the launch duration."""
+    if bound == "mfma":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, peak_tflops, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    out = {"kernel": unit_name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": recorded_traffic(unit_name), "ms": round(ms, 4)}
+    if algorithmic_bytes is not None:
+        out["algorithmic_bytes"] = algorithmic_bytes
+    cnt = recorded_counters(unit_name)
+    if cnt is not None:
+        out["counters"] = cnt
+    return out
+
+
+def fwd_algorithmic_bytes(B, Hq, Hkv, T, d):
+    """HBM bytes the forward cannot avoid: read Q, K, V once, write O and the LSE."""
+    return 2 * B * Hq * T * d * 2 + 2 * B * Hkv * T * d * 2 + 4 * B * Hq * T
+
+
+def bwd_algorithmic_bytes(B, Hq, Hkv, T, d):
+    """HBM bytes the backward cannot avoid: read Q, O, dO, LSE and K, V once,
+    write dQ, dK, dV, plus the per-row statistics (written once by the dQ
+    kernel, read once by the dK/dV kernel)."""
+    q_like = B * Hq * T * d * 2
+    kv_like = B * Hkv * T * d * 2
+    rows = B * Hq * T
+    return 3 * q_like + 2 * kv_like + 4 * rows + q_like + 2 * kv_like + 2 * 8 * rows
+
+
+def _attention_buffers(dev, backward):
+    import torch
+    from io_aware_softmax_05_amd import fa
+    q, k = dev["q"], dev["k"]
+    B, Hq, T, d = q.shape
+    bufs = {"o": torch.empty_like(q), "lse": torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")}
+    if backward:
+        bufs.update(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(k))
+        n = fa.fa_bwd_workspace_size(B, Hq, T, d)
+        bufs["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda")
+        bufs["ws_bytes"] = n
+    return bufs
+
+
+def attention_calls(dev, causal, backward, p_drop=0.0, seed=0, offset=0):
+    """[(name, fn)] for the forward (and backward) of one layer on device inputs."""
+    from io_aware_softmax_05_amd import fa
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    scale = d ** -0.5
+    b = _attention_buffers(dev, backward)
+
+    def f():
+        if p_drop > 0:
+            fa.fa_fwd_dropout(q, k, v, b["o"], b["lse"], B, Hq, Hkv, T, T, d, scale, causal, p_drop, seed, offset)
+        else:
+            fa.fa_fwd(q, k, v, b["o"], b["lse"], B, Hq, Hkv, T, T, d, scale, causal)
+
+    calls = [("fwd", f)]
+    if backward:
+        do = dev["do"]
+
+        def g():
+            args = (q, k, v, b["o"], do, b["lse"], b["dq"], b["dk"], b["dv"], b["ws"], b["ws_bytes"],
+                    B, Hq, Hkv, T, T, d, scale, causal)
+            if p_drop > 0:
+                fa.fa_bwd_dropout(*args, p_drop, seed, offset)
+            else:
+                fa.fa_bwd(*args)
+        calls.append(("bwd", g))
+    return calls
 
 
 DROPOUT_P = 0.1                # attention dropout of the GPT-2-medium layer with dropout
 DROPOUT_SEED, DROPOUT_OFFSET = 0x5EED, 0
 
 
-def run_attention(name, steps, warmup, backward=True, p_drop=0.0):
+def _randn_bf16(shape, gen):
+    import torch
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def run_decode(raw, steps, warmup):
+    """Split-KV decode on the seeded cache; a device copy of it is used on
+    alternate calls so that no call finds the previous call's rows in the MALL."""
     import torch
     from io_aware_softmax_05_amd import fa
-    B, Hq, Hkv, T, d, causal, seed = WORKLOADS[name]
-    scale = d ** -0.5
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(seed)
-    q = _randn_bf16((B, Hq, T, d), gen)
-    k = _randn_bf16((B, Hkv, T, d), gen)
-    v = _randn_bf16((B, Hkv, T, d), gen)
-    do = _randn_bf16((B, Hq, T, d), gen)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = fa.fa_bwd_workspace_size(B, Hq, T, d)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    t_fwd, t_bwd = Timer(stream), Timer(stream)
-
-    def f():
-        if p_drop > 0:
-            fa.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, p_drop, DROPOUT_SEED,
-                              DROPOUT_OFFSET, stream)
-        else:
-            fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, T, T, d, scale, causal, stream)
-
-    def b():
-        if p_drop > 0:
-            fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, scale, causal,
-                              p_drop, DROPOUT_SEED, DROPOUT_OFFSET, stream)
-        else:
-            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, scale, causal, stream)
-
-    for _ in range(warmup):
-        f()
-        if backward:
-            b()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        t_fwd.record(f)
-        if backward:
-            t_bwd.record(b)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ff = fwd_flops(B, Hq, T, T, d, causal)
-    res = {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "d": d, "causal": causal,
-           "wall_s": wall, "ms_per_step": wall * 1e3 / steps,
-           "fwd_ms": t_fwd.mean_ms(), "fwd_median_ms": t_fwd.median_ms(), "fwd_flop": ff,
-           "step_flop": ff * (3.5 if backward else 1.0)}
-    if backward:
-        res["bwd_ms"] = t_bwd.mean_ms()
-        res["bwd_median_ms"] = t_bwd.median_ms()
-        res["bwd_flop"] = 2.5 * ff
-    res["host"] = {"q": q, "k": k, "v": v, "do": do}
-    return res
-
-
-def run_decode(steps, warmup):
-    import torch
-    from io_aware_softmax_05_amd import fa, inputs
-    B, Hq, Hkv, Tk_max, d = (DECODE[k] for k in ("B", "Hq", "Hkv", "Tk_max", "d"))
-    lens_np = inputs.decode_lengths(inputs.make_rng(DECODE["seed"]), B)
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(DECODE["seed"])
-    q = _randn_bf16((B, Hq, d), gen)
-    # two cache copies (1 GiB per tensor each), used in turn, so that no call
-    # finds the previous call's rows in the 256 MiB MALL
-    caches = [(_randn_bf16((B, Hkv, Tk_max, d), gen), _randn_bf16((B, Hkv, Tk_max, d), gen)) for _ in range(2)]
-    lens = torch.from_numpy(lens_np).cuda()
+    dev = to_device({n: raw[n] for n in ("q", "k", "v")})
+    lens = torch.from_numpy(raw["seq_lens"]).cuda()
+    q = dev["q"]
+    B, Hq, d = q.shape
+    Hkv, Tk_max = dev["k"].shape[1], dev["k"].shape[2]
+    caches = [(dev["k"], dev["v"]), (dev["k"].clone(), dev["v"].clone())]
     ws_bytes = fa.fa_decode_workspace_size(B, Hq, Tk_max, d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    t = Timer(stream)
-
     turn = [0]
 
     def call():
         kc, vc = caches[turn[0] & 1]
         turn[0] += 1
-        fa.fa_decode_splitkv(q, kc, vc, lens, o, lse, ws, ws_bytes, B, Hq, Hkv, Tk_max, d, d ** -0.5, 0, stream)
+        fa.fa_decode_splitkv(q, kc, vc, lens, o, lse, ws, ws_bytes, B, Hq, Hkv, Tk_max, d, d ** -0.5, 0)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        t.record(call)
-    torch.cuda.synchronize()
-    kv_bytes = float(lens_np.astype(np.int64).sum()) * Hkv * 2 * d * 2
+    _, t = timed([("dec", call)], steps, warmup, torch.cuda.current_stream())
+    kv_bytes = float(raw["seq_lens"].astype(np.int64).sum()) * Hkv * 2 * d * 2
     io_bytes = 2.0 * B * Hq * d * 2
-    return {"ms": t.mean_ms(), "median_ms": t.median_ms(), "bytes": kv_bytes + io_bytes,
-            "sum_lengths": int(lens_np.sum())}
+    return {"median_ms": t["dec"].median_ms(), "bytes": kv_bytes + io_bytes, "sum_lengths": int(raw["seq_lens"].sum())}
 
 
 def window_pairs(T, W):
@@ -285,34 +348,19 @@ def run_window(steps, warmup):
     B, Hq, Hkv, T, d, W = 1, 32, 8, 32768, 128, 4096
     gen = torch.Generator(device="cuda")
     gen.manual_seed(6)
-    q = _randn_bf16((B, Hq, T, d), gen)
-    k = _randn_bf16((B, Hkv, T, d), gen)
-    v = _randn_bf16((B, Hkv, T, d), gen)
-    do = _randn_bf16((B, Hq, T, d), gen)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = fa.fa_bwd_workspace_size(B, Hq, T, d)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    t_f, t_b = Timer(stream), Timer(stream)
+    q, k, v, do = (_randn_bf16(s, gen) for s in ((B, Hq, T, d), (B, Hkv, T, d), (B, Hkv, T, d), (B, Hq, T, d)))
+    b = _attention_buffers({"q": q, "k": k}, True)
 
     def f():
-        fa.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, T, T, d, d ** -0.5, W, stream)
+        fa.fa_fwd_window(q, k, v, b["o"], b["lse"], B, Hq, Hkv, T, T, d, d ** -0.5, W)
 
-    def b():
-        fa.fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, T, T, d, d ** -0.5, W, stream)
+    def g():
+        fa.fa_bwd_window(q, k, v, b["o"], do, b["lse"], b["dq"], b["dk"], b["dv"], b["ws"], b["ws_bytes"],
+                         B, Hq, Hkv, T, T, d, d ** -0.5, W)
 
-    for _ in range(warmup):
-        f()
-        b()
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        t_f.record(f)
-        t_b.record(b)
-    torch.cuda.synchronize()
+    _, t = timed([("fwd", f), ("bwd", g)], steps, warmup, torch.cuda.current_stream())
     ff = 4.0 * d * window_pairs(T, W) * B * Hq
-    return {"fwd_ms": t_f.median_ms(), "bwd_ms": t_b.median_ms(), "fwd_flop": ff, "bwd_flop": 2.5 * ff}
+    return {"fwd_ms": t["fwd"].median_ms(), "bwd_ms": t["bwd"].median_ms(), "fwd_flop": ff, "bwd_flop": 2.5 * ff}
 
 
 def run_fp8(steps, warmup):
@@ -335,102 +383,215 @@ def run_fp8(steps, warmup):
     vt8 = v8.transpose(2, 3).contiguous()
     o = torch.empty((B, H, T, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    t = Timer(stream)
 
     def call():
-        fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o, lse, B, H, H, T, T, d, d ** -0.5, True, stream)
+        fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o, lse, B, H, H, T, T, d, d ** -0.5, True)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        t.record(call)
-    torch.cuda.synchronize()
-    return {"median_ms": t.median_ms(), "flop": fwd_flops(B, H, T, T, d, True)}
+    _, t = timed([("fp8", call)], steps, warmup, torch.cuda.current_stream())
+    return {"median_ms": t["fp8"].median_ms(), "flop": fwd_flops(B, H, T, T, d, True)}
 
 
-def run_small_f32(steps, warmup):
+def run_small_f32(raw, steps, warmup):
     """The single-head fp32 workload (B1 H1 T256 d64): latency only."""
     import torch
     from io_aware_softmax_05_amd import fa
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(1)
-    q, k, v = (torch.randn((1, 1, 256, 64), generator=gen, device="cuda", dtype=torch.float32) for _ in range(3))
+    dev = to_device(raw)
+    q, k, v = dev["q"], dev["k"], dev["v"]
     o = torch.empty_like(q)
     lse = torch.empty((1, 1, 256), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    t = Timer(stream)
 
     def call():
-        fa.fa_fwd_f32(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 0.125, False, stream)
+        fa.fa_fwd_f32(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 0.125, False)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        t.record(call)
-    torch.cuda.synchronize()
-    return {"median_ms": t.median_ms(), "flop": fwd_flops(1, 1, 256, 256, 64, False)}
+    _, t = timed([("f32", call)], steps, warmup, torch.cuda.current_stream())
+    return {"median_ms": t["f32"].median_ms(), "flop": fwd_flops(1, 1, 256, 256, 64, False)}
 
 
-def roofline(bound, work, ms, unit_name, algorithmic_bytes=None, peak_tflops=PEAK_BF16_TFLOPS):
-    """Roofline entry for one launch unit: `work` is FLOP (bound "mfma", against
-    the matrix peak of the unit's dtype) or bytes (bound "hbm") per launch, `ms`
-    the mean launch duration."""
-    if bound == "mfma":
-        achieved, peak, unit = work / (ms * 1e-3) / 1e12, peak_tflops, "TFLOP/s"
-    else:
-        achieved, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-    out = {"kernel": unit_name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-           "frac": round(achieved / peak, 4), "traffic": recorded_traffic(unit_name), "ms": round(ms, 4)}
-    if algorithmic_bytes is not None:
-        out["algorithmic_bytes"] = algorithmic_bytes
-    return out
+# ------------------------------------------------------------ clock reading
 
+def read_sclk_under_load(launch, seconds=2.0):
+    """Engine clock reported by amd-smi while `launch` (the headline kernel) is
+    issued back to back: the matrix peak assumes the 2400 MHz top clock, and
+    sustained matrix work runs below it. Returns {"mhz": [...], ...} or an error."""
+    import torch
+    box = {}
 
-def bwd_algorithmic_bytes(B, Hq, Hkv, T, d):
-    """HBM bytes the backward cannot avoid: read Q, O, dO, LSE and K, V once,
-    write dQ, dK, dV, plus the per-row statistics (written once by the dQ
-    kernel, read once by the dK/dV kernel)."""
-    q_like = B * Hq * T * d * 2
-    kv_like = B * Hkv * T * d * 2
-    rows = B * Hq * T
-    return 3 * q_like + 2 * kv_like + 4 * rows + q_like + 2 * kv_like + 2 * 8 * rows
+    def reader():
+        time.sleep(0.5)   # let the clock settle under the load
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                               text=True, timeout=20)
+            box["out"], box["rc"] = r.stdout, r.returncode
+        except Exception as e:  # noqa: BLE001 - reported, never fatal
+            box["err"] = repr(e)
+
+    th = threading.Thread(target=reader)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < 30:
+        for _ in range(50):
+            launch()
+        torch.cuda.synchronize()
+    th.join()
+    if "err" in box or box.get("rc", 1) != 0:
+        return {"mhz": None, "error": box.get("err") or f"amd-smi rc {box.get('rc')}"}
+    mhz = []
+
+    def walk(x, key=""):
+        if isinstance(x, dict):
+            for kk, vv in x.items():
+                if kk == "clk" and key.lower().startswith("gfx"):
+                    val = vv.get("value") if isinstance(vv, dict) else vv
+                    try:
+                        mhz.append(float(val))
+                    except (TypeError, ValueError):
+                        pass
+                else:
+                    walk(vv, kk if isinstance(vv, dict) else key)
+        elif isinstance(x, list):
+            for vv in x:
+                walk(vv, key)
+    try:
+        walk(json.loads(box["out"]))
+    except ValueError:
+        return {"mhz": None, "error": "amd-smi output is not JSON"}
+    return {"mhz": mhz or None, "source": "amd-smi metric --clock, sampled while the headline kernel runs"}
 
 
 # ------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(res, seconds):
-    """The fp64 oracle, untouched, on whole (batch, head) slices of the same
-    workload until about `seconds` of CPU work; reported in the step's unit."""
+def _pool_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)   # one BLAS thread per worker process: the pool supplies the parallelism
+
+
+def _oracle_job(job):
+    """One unit of oracle work in a worker process (imports no GPU code)."""
+    from io_aware_softmax_05_amd import inputs
     from oracle import attention_ref as ref
+    kind = job[0]
+    if kind == "fwd":          # one head: q [Tq,d], k, v [Tk,d] bit patterns or fp32
+        _, q, k, v, scale, causal = job
+        ref.attention_fwd(inputs.widen(q)[None, None], inputs.widen(k)[None, None], inputs.widen(v)[None, None],
+                          scale, causal)
+    elif kind == "fwdbwd":     # one head, forward then backward
+        _, q, k, v, do, scale, causal = job
+        qq, kk, vv, dd = (inputs.widen(x)[None, None] for x in (q, k, v, do))
+        ref.attention_fwd(qq, kk, vv, scale, causal)
+        ref.attention_bwd(qq, kk, vv, dd, scale, causal)
+    elif kind == "fwd_rows":   # some rows of one head
+        _, q, k, v, rows, scale, causal = job
+        ref.attention_fwd(inputs.widen(q)[None, None], inputs.widen(k)[None, None], inputs.widen(v)[None, None],
+                          scale, causal, rows=rows)
+    elif kind == "decode":     # one batch entry: q [Hq,d], caches [Hkv,L,d]
+        _, q, k, v, L, scale = job
+        ref.decode(inputs.widen(q)[None], inputs.widen(k)[None], inputs.widen(v)[None], np.array([L]), scale)
+    else:
+        raise ValueError(kind)
+    return 0
+
+
+def _pool_wall(pool, jobs):
+    t0 = time.perf_counter()
+    list(pool.imap_unordered(_oracle_job, jobs, chunksize=1))
+    return time.perf_counter() - t0
+
+
+def host_info():
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = len(os.sched_getaffinity(0))
-    B, Hq, Hkv, T, d, causal = (res[k] for k in ("B", "Hq", "Hkv", "T", "d", "causal"))
-    h = res["host"]
-    g = Hq // Hkv
-    scale = d ** -0.5
-    done, t0 = 0, time.perf_counter()
-    while True:
-        b, hq = divmod(done, Hq)
-        hk = hq // g
-        sl = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)  # noqa: E731
-        qh, kh, vh, doh = sl(h["q"], hq), sl(h["k"], hk), sl(h["v"], hk), sl(h["do"], hq)
-        ref.attention_fwd(qh, kh, vh, scale, causal)
-        ref.attention_bwd(qh, kh, vh, doh, scale, causal)
-        done += 1
-        if time.perf_counter() - t0 >= seconds or done >= B * Hq:
-            break
-    elapsed = time.perf_counter() - t0
-    per_head_flop = res["step_flop"] / (B * Hq)
-    return {"value": per_head_flop * done / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} of {B * Hq} (batch, head) slices of the step's workload, fp64 numpy fwd+bwd, "
-                      f"{elapsed:.1f} s wall"}
+        blas = [{k: i.get(k) for k in ("internal_api", "version", "architecture", "num_threads")}
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # noqa: BLE001 - informational
+        pass
+    return {"cpu_model": cpu, "blas": blas, "affinity_cores": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__}
+
+
+def cpu_baseline(raw, full=False):
+    """The fp64 oracle, untouched, timed on the host cores: one job per head
+    (or batch entry), spread over a pool of worker processes with one BLAS
+    thread each. The headline (`value`) is the whole causal B1 H32 T8192 d128
+    forward, median of 3 passes; the other workloads are reported beside it."""
+    import multiprocessing as mp
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")          # workers never touch the GPU
+    out = {"unit": "TFLOP/s", "cores": cores, "kind": "oracle"}
+    out.update(host_info())
+    cfg = {}
+    with ctx.Pool(cores, initializer=_pool_init) as pool:
+        pool.map(_oracle_job, [("fwd", np.zeros((2, 64), np.float32), np.zeros((2, 64), np.float32),
+                                np.zeros((2, 64), np.float32), 0.1, False)] * cores)   # start the workers
+        # headline: the whole causal 8k forward, every head
+        r3 = raw[3]
+        w3 = INPUT_WORKLOADS[3]
+        jobs = [("fwd", r3["q"][0, h], r3["k"][0, h], r3["v"][0, h], w3.scale, True) for h in range(w3.Hq)]
+        walls = [_pool_wall(pool, jobs) for _ in range(3)]
+        flop3 = fwd_flops(1, w3.Hq, w3.Tq, w3.Tk, w3.d, True)
+        out["value"] = round(flop3 / float(np.median(walls)) / 1e12, 5)
+        out["sample"] = (f"the whole {w3.name} (all {w3.Hq} heads, seeded inputs), fp64 numpy three-step oracle, "
+                         f"one head per job on {cores} worker processes with one BLAS thread each; median of 3 "
+                         f"passes: {', '.join(f'{x:.2f}' for x in walls)} s")
+        # single-head fp32 workload: whole, median of 3
+        r1, w1 = raw[1], INPUT_WORKLOADS[1]
+        walls = [_pool_wall(pool, [("fwd", r1["q"][0, 0], r1["k"][0, 0], r1["v"][0, 0], w1.scale, False)])
+                 for _ in range(3)]
+        cfg[w1.name] = {"median_s": round(float(np.median(walls)), 5), "passes": 3, "whole_workload": True}
+        # GPT-2-medium layer fwd+bwd: whole (1024 heads)
+        r2, w2 = raw[2], INPUT_WORKLOADS[2]
+        jobs = [("fwdbwd", r2["q"][b, h], r2["k"][b, h], r2["v"][b, h], r2["do"][b, h], w2.scale, False)
+                for b in range(w2.B) for h in range(w2.Hq)]
+        walls = [_pool_wall(pool, jobs) for _ in range(3 if full else 1)]
+        flop2 = 3.5 * fwd_flops(w2.B, w2.Hq, w2.Tq, w2.Tk, w2.d, False)
+        cfg[w2.name] = {"median_s": round(float(np.median(walls)), 3), "passes": len(walls),
+                        "TFLOP/s": round(flop2 / float(np.median(walls)) / 1e12, 5), "whole_workload": True}
+        # split-KV decode: whole (16 batch entries, their cached prefixes)
+        r5, w5 = raw[5], INPUT_WORKLOADS[5]
+        lens = r5["seq_lens"]
+        jobs = [("decode", r5["q"][b], r5["k"][b, :, :int(lens[b])], r5["v"][b, :, :int(lens[b])], int(lens[b]),
+                 w5.scale) for b in range(w5.B)]
+        walls = [_pool_wall(pool, jobs) for _ in range(3)]
+        dec_bytes = float(lens.astype(np.int64).sum()) * w5.Hkv * 2 * w5.d * 2 + 2.0 * w5.B * w5.Hq * w5.d * 2
+        cfg[w5.name] = {"median_s": round(float(np.median(walls)), 4), "passes": 3,
+                        "GB/s": round(dec_bytes / float(np.median(walls)) / 1e9, 4), "whole_workload": True}
+        # causal 32k GQA layer
+        r4, w4 = raw[4], INPUT_WORKLOADS[4]
+        g = w4.Hq // w4.Hkv
+        heads = [(hk * g + i, hk) for hk in (0, w4.Hkv - 1) for i in range(g)]   # KV groups 0 and 7
+        flop4 = fwd_flops(1, w4.Hq, w4.Tq, w4.Tk, w4.d, True)
+        if full:
+            jobs = [("fwdbwd", r4["q"][0, h], r4["k"][0, hk], r4["v"][0, hk], r4["do"][0, h], w4.scale, True)
+                    for h, hk in heads]
+            wall = _pool_wall(pool, jobs)
+            cfg[w4.name] = {"s_for_kv_groups_0_and_7": round(wall, 2), "extrapolated_s": round(wall * w4.Hkv / 2, 1),
+                            "TFLOP/s": round(3.5 * flop4 / (wall * w4.Hkv / 2) / 1e12, 5),
+                            "extrapolation": f"fwd+bwd of the {len(heads)} query heads of KV groups 0 and 7 timed in "
+                                             f"full, scaled x{w4.Hkv // 2} to all {w4.Hkv} groups (heads are "
+                                             "independent)"}
+        else:
+            rows = np.arange(0, w4.Tq, w4.Tq // 256)   # 256 evenly spaced rows per head
+            jobs = [("fwd_rows", r4["q"][0, h], r4["k"][0, hk], r4["v"][0, hk], rows, w4.scale, True)
+                    for h, hk in heads]
+            wall = _pool_wall(pool, jobs)
+            scale_up = (w4.Tq / len(rows)) * (w4.Hq / len(heads))
+            cfg[w4.name] = {"fwd_rows_s": round(wall, 2), "fwd_extrapolated_s": round(wall * scale_up, 1),
+                            "fwd_TFLOP/s": round(flop4 / (wall * scale_up) / 1e12, 5),
+                            "extrapolation": f"forward of 256 evenly spaced full-length rows of each of the "
+                                             f"{len(heads)} query heads of KV groups 0 and 7 (the oracle computes "
+                                             f"every key of a row, masked or not), scaled x{scale_up:g} to the whole "
+                                             "forward; the backward is timed only with --cpu-full"}
+    out["configs"] = cfg
+    return out
 
 
 # ----------------------------------------------------------- counter records
@@ -477,6 +638,18 @@ def _counter_means(path, counter):
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
+def _match_unit_kernels(table, unit):
+    """(kernel key, grid) entries of a counter table that make up `unit`."""
+    found = []
+    for spec in TRAFFIC_UNITS[unit]:
+        k, _, grid = spec.partition("@")
+        hits = [nk for nk in table if nk[0] == k and (not grid or nk[1] == int(grid))]
+        if len(hits) != 1:
+            return None
+        found.append(hits[0])
+    return found
+
+
 def record_traffic(d):
     def one(name, counter):
         paths = glob.glob(os.path.join(d, name, "*counter_collection.csv"))
@@ -484,6 +657,7 @@ def record_traffic(d):
             raise SystemExit(f"missing {name}/*counter_collection.csv under {d}")
         return _counter_means(paths[0], counter)
     fetch, write = one("fetch_all", "FETCH_SIZE"), one("write_all", "WRITE_SIZE")
+
     def copy_value(m):
         vals = [v for (n, _), v in m.items() if n == "copy"]
         if len(vals) != 1:
@@ -492,15 +666,12 @@ def record_traffic(d):
     cf, cw = copy_value(one("fetch_copy", "FETCH_SIZE")), copy_value(one("write_copy", "WRITE_SIZE"))
     f_fac, w_fac = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
     units = {}
-    for unit, kernels in TRAFFIC_UNITS.items():
-        ks = {}
-        total = 0.0
-        for spec in kernels:
-            k, _, grid = spec.partition("@")
-            hits = [nk for nk in fetch if nk[0] == k and (not grid or nk[1] == int(grid))]
-            if len(hits) != 1:
-                raise SystemExit(f"{len(hits)} counter records match kernel {spec}: {hits}")
-            nk = hits[0]
+    for unit in TRAFFIC_UNITS:
+        hits = _match_unit_kernels(fetch, unit)
+        if hits is None:
+            raise SystemExit(f"the counter records do not match the kernels of {unit}")
+        ks, total = {}, 0.0
+        for nk in hits:
             ks[f"{nk[0]} grid {nk[1]}"] = {"fetch_kib": round(fetch[nk], 1), "write_kib": round(write.get(nk, 0.0), 1)}
             total += fetch[nk] * 1024 * f_fac + write.get(nk, 0.0) * 1024 * w_fac
         units[unit] = {"bytes": round(total), "source_sha256": unit_source_hash(unit), "kernels": ks}
@@ -515,52 +686,158 @@ def record_traffic(d):
     return 0
 
 
+# Instruction and cycle counters (rocprofv3 --pmc passes of at most 8 SQ
+# counters each). Per-dispatch values are sums over the 8 XCDs and their SIMDs;
+# GRBM_GUI_ACTIVE counts each XCD's busy clocks, so GRBM_GUI_ACTIVE / 8 over
+# the dispatch's duration is the engine clock it ran at.
+COUNTER_PASSES = [
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
+     "SQ_INSTS_VALU", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+     "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_INSTS_VALU_TRANS_F32", "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+     "SQ_WAVES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_ACTIVE_INST_MISC", "GRBM_GUI_ACTIVE"],
+]
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def _counter_table(paths):
+    """{(kernel key, grid): {counter: mean per dispatch, "_duration_s": mean}} over counter CSVs."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    durs = collections.defaultdict(dict)
+    for path in paths:
+        tag = os.path.dirname(path)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if not name.startswith("void fa::"):
+                    continue
+                key = (kernel_key(name), int(r["Grid_Size"]))
+                did = (tag, r["Dispatch_Id"])
+                vals[key][r["Counter_Name"]][did] += float(r["Counter_Value"])
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    durs[key][did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    out = {}
+    for key, cs in vals.items():
+        out[key] = {c: sum(v.values()) / len(v) for c, v in cs.items()}
+        if durs[key]:
+            out[key]["_duration_s"] = sum(durs[key].values()) / len(durs[key])
+    return out
+
+
+def derived_counters(c):
+    """Fractions of the kernel's time (per SIMD or CU) from one kernel's counter means."""
+    g = c.get("GRBM_GUI_ACTIVE")
+    d = {}
+    if not g:
+        return d
+    cyc = g / N_XCD                                   # busy clocks of one XCD
+    if c.get("_duration_s"):
+        d["clock_mhz"] = round(cyc / c["_duration_s"] / 1e6)
+        d["duration_us_under_counters"] = round(c["_duration_s"] * 1e6, 1)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        d["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD), 4)
+        if c["SQ_VALU_MFMA_BUSY_CYCLES"] > 0 and "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+            d["valu_coexec_of_mfma_busy"] = round(c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+    if "SQ_ACTIVE_INST_VALU" in c:                   # quad-cycles summed over a CU's 4 SIMDs
+        d["valu_busy"] = round(c["SQ_ACTIVE_INST_VALU"] / (cyc * N_CU), 4)
+    if "SQ_LDS_IDX_ACTIVE" in c:
+        d["lds_busy"] = round(c["SQ_LDS_IDX_ACTIVE"] / (cyc * N_CU), 4)
+    if c.get("SQ_WAVE_CYCLES"):
+        for k, name in (("SQ_WAIT_ANY", "wave_waiting"), ("SQ_WAIT_INST_ANY", "wave_waiting_for_issue"),
+                        ("SQ_WAIT_INST_LDS", "wave_waiting_for_lds_issue")):
+            if k in c:
+                d[name] = round(c[k] / c["SQ_WAVE_CYCLES"], 4)
+    m = c.get("SQ_INSTS_MFMA")
+    if m:
+        if "SQ_INSTS_VALU" in c:
+            d["valu_insts_per_mfma"] = round((c["SQ_INSTS_VALU"] - m) / m, 3)
+        for k, name in (("SQ_INSTS_VALU_TRANS_F32", "exp_log_insts_per_mfma"), ("SQ_INSTS_LDS", "lds_insts_per_mfma"),
+                        ("SQ_INSTS_SALU", "salu_insts_per_mfma")):
+            if k in c:
+                d[name] = round(c[k] / m, 3)
+    for k, name in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", "mfma_bf16_flop"), ("SQ_INSTS_VALU_MFMA_MOPS_F8", "mfma_fp8_flop")):
+        if c.get(k):
+            d[name] = c[k] * 512
+    if "SQ_LDS_BANK_CONFLICT" in c:
+        d["lds_bank_conflict_cycles"] = c["SQ_LDS_BANK_CONFLICT"]
+    return d
+
+
+def record_counters(d):
+    paths = sorted(glob.glob(os.path.join(d, "*", "*counter_collection.csv")))
+    if not paths:
+        raise SystemExit(f"no */*counter_collection.csv under {d}")
+    table = _counter_table(paths)
+    units = {}
+    for unit in TRAFFIC_UNITS:
+        hits = _match_unit_kernels(table, unit)
+        if hits is None:
+            continue
+        ks = {f"{k} grid {g}": {"derived": derived_counters(table[(k, g)]),
+                                "counters": {c: round(v, 1) for c, v in sorted(table[(k, g)].items())}}
+              for k, g in hits}
+        units[unit] = {"source_sha256": unit_source_hash(unit), "kernels": ks,
+                       "derived": {kk: vv["derived"] for kk, vv in ks.items()}}
+    rec = {"note": "rocprofv3 --pmc passes (see profiles/counters.md); fractions are of the kernel's busy clocks",
+           "passes": COUNTER_PASSES, "units": units}
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({u: v["derived"] for u, v in units.items()}, indent=1))
+    return 0
+
+
 # ---------------------------------------------------------------------- main
 
+INPUT_WORKLOADS = None   # inputs.WORKLOADS, bound in main() (workers import it themselves)
+
+
 def main():
+    global INPUT_WORKLOADS
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the causal 8k and decode measurements")
-    ap.add_argument("--only", choices=["step", "causal-8k-fwd", "causal-8k-fp8", "decode", "dropout", "copy"],
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="oracle baseline with the GPT-2-medium layer in 3 passes and the 32k GQA layer's fwd+bwd "
+                         "for KV groups 0 and 7 in full (minutes of CPU time)")
+    ap.add_argument("--no-extras", action="store_true", help="headline only")
+    ap.add_argument("--only", choices=["headline", "step", "gqa32k", "decode", "dropout", "fp8", "window", "f32",
+                                       "copy"],
                     help="run one measurement alone (profiling runs); 'copy' runs a plain device copy "
                          "of 1 GiB, the calibration for HBM byte counters")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
+    ap.add_argument("--record-counters", metavar="DIR",
+                    help="write profiles/counters.json from rocprofv3 --pmc passes in DIR/<pass>/ (no GPU needed)")
+    ap.add_argument("--print-counter-passes", action="store_true",
+                    help="print the counter passes, one comma-separated line each (for the profiling commands)")
     args = ap.parse_args()
+    if args.print_counter_passes:
+        for p in COUNTER_PASSES:
+            print(",".join(p))
+        return 0
     if args.record_traffic:
         return record_traffic(args.record_traffic)
+    if args.record_counters:
+        return record_counters(args.record_counters)
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only (there is no multi-GPU path); --gpus must be 1"}))
         return 2
 
     import torch
-    from io_aware_softmax_05_amd import fa
+    from io_aware_softmax_05_amd import fa, inputs
+    INPUT_WORKLOADS = inputs.WORKLOADS
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         return 2
     fa.load_library()
     torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    W = inputs.WORKLOADS
 
-    if args.only == "causal-8k-fwd":
-        r = run_attention("causal-8k-fwd", args.steps, args.warmup, backward=False)
-        r.pop("host")
-        print(json.dumps(r), flush=True)
-        return 0
-    if args.only == "causal-8k-fp8":
-        print(json.dumps(run_fp8(args.steps, args.warmup)), flush=True)
-        return 0
-    if args.only == "decode":
-        print(json.dumps(run_decode(args.steps, args.warmup)), flush=True)
-        return 0
-    if args.only == "dropout":
-        r = run_attention("gpt2-medium-fwd-bwd", args.steps, args.warmup, backward=True, p_drop=DROPOUT_P)
-        r.pop("host")
-        print(json.dumps(r), flush=True)
-        return 0
     if args.only == "copy":
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -570,69 +847,119 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": max(1, args.steps)}), flush=True)
         return 0
-    if args.only == "step":
-        args.no_extras = True
-        args.no_cpu_baseline = True
 
-    res = run_attention("gpt2-medium-fwd-bwd", args.steps, args.warmup, backward=True)
-    B, Hq, Hkv, T, d = (res[k] for k in ("B", "Hq", "Hkv", "T", "d"))
-    value = res["step_flop"] / (res["ms_per_step"] * 1e-3) / 1e12
-    out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "GPT-2-medium attention layer fwd+bwd", "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "seq_len": T, "head_dim": d, "causal": res["causal"], "step": "fa_fwd + fa_bwd",
-                   "flop_per_step": res["step_flop"]},
-        # the dominant launch of the step: fa_bwd (its two kernels)
-        "roofline": roofline("mfma", res["bwd_flop"], res["bwd_ms"], "fa_bwd B64 H16 T1024 d64",
-                             bwd_algorithmic_bytes(B, Hq, Hkv, T, d)),
-        "phases": {"fa_fwd": roofline("mfma", res["fwd_flop"], res["fwd_ms"], "fa_fwd B64 H16 T1024 d64")},
-    }
-    if not args.no_extras:
+    want = (lambda name: args.only is None or args.only == name)
+    extras = not args.no_extras and args.only is None
+    raw = {}
+    if want("headline") or not args.no_cpu_baseline:
+        raw[3] = inputs.workload_inputs(W[3])
+    out = {"targets": {}}
+
+    # ---- targets (before the headline; their inputs are freed afterwards)
+    if extras or want("step"):
+        raw[2] = inputs.workload_inputs(W[2])
+        w = W[2]
+        dev = to_device(raw[2])
+        wall, t = timed(attention_calls(dev, w.causal, True), 20, 5, stream)
+        ff = fwd_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
+        out["targets"]["GPT-2-medium fwd+bwd B64 H16 T1024 d64 step"] = {
+            "ms_per_step": round(wall * 1e3 / 20, 4), "TFLOP/s": round(3.5 * ff / (wall / 20) / 1e12, 2)}
+        out["targets"]["fa_fwd B64 H16 T1024 d64"] = roofline(
+            "mfma", ff, t["fwd"].median_ms(), "fa_fwd B64 H16 T1024 d64",
+            fwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d))
+        out["targets"]["fa_bwd B64 H16 T1024 d64"] = roofline(
+            "mfma", 2.5 * ff, t["bwd"].median_ms(), "fa_bwd B64 H16 T1024 d64",
+            bwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d))
+        del dev
         torch.cuda.empty_cache()
-        # the targets: 10 untimed launches, then the median of 50 timed ones
-        tgt = run_attention("causal-8k-fwd", 50, 10, backward=False)
-        tgt.pop("host")
-        out["targets"] = {"fa_fwd causal B1 H32 T8192 d128":
-                          roofline("mfma", tgt["fwd_flop"], tgt["fwd_median_ms"], "fa_fwd causal B1 H32 T8192 d128")}
-        torch.cuda.empty_cache()
-        dec = run_decode(50, 10)
-        out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"] = roofline(
-            "hbm", dec["bytes"], dec["median_ms"], "fa_decode_splitkv B16 Hq32 Hkv8 d128", dec["bytes"])
-        out["targets"]["fa_decode_splitkv B16 Hq32 Hkv8 d128"]["sum_lengths"] = dec["sum_lengths"]
-        torch.cuda.empty_cache()
-        g32 = run_attention("causal-32k-gqa-fwd-bwd", 3, 1, backward=True)
-        g32.pop("host")
+    if extras or want("gqa32k"):
+        raw[4] = inputs.workload_inputs(W[4])
+        w = W[4]
+        dev = to_device(raw[4])
+        _, t = timed(attention_calls(dev, w.causal, True), 3, 1, stream)
+        ff = fwd_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
         out["targets"]["fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128"] = roofline(
-            "mfma", g32["fwd_flop"], g32["fwd_ms"], "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128")
+            "mfma", ff, t["fwd"].median_ms(), "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128",
+            fwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d))
         out["targets"]["fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128"] = roofline(
-            "mfma", g32["bwd_flop"], g32["bwd_ms"], "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128")
+            "mfma", 2.5 * ff, t["bwd"].median_ms(), "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128",
+            bwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d))
+        del dev
         torch.cuda.empty_cache()
+    if extras or want("decode"):
+        raw[5] = inputs.workload_inputs(W[5])
+        dec = run_decode(raw[5], 50, 10)
+        u = "fa_decode_splitkv B16 Hq32 Hkv8 d128"
+        out["targets"][u] = roofline("hbm", dec["bytes"], dec["median_ms"], u, dec["bytes"])
+        out["targets"][u]["sum_lengths"] = dec["sum_lengths"]
+        torch.cuda.empty_cache()
+    if extras or want("window"):
         sw = run_window(5, 2)
-        out["targets"]["fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128"] = roofline(
-            "mfma", sw["fwd_flop"], sw["fwd_ms"], "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128")
-        out["targets"]["fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128"] = roofline(
-            "mfma", sw["bwd_flop"], sw["bwd_ms"], "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128")
+        for ph in ("fwd", "bwd"):
+            u = f"fa_{ph}_window B1 Hq32 Hkv8 T32768 W4096 d128"
+            out["targets"][u] = roofline("mfma", sw[f"{ph}_flop"], sw[f"{ph}_ms"], u)
         torch.cuda.empty_cache()
+    if extras or want("fp8"):
         f8 = run_fp8(50, 10)
-        out["targets"]["fa_fwd_fp8 causal B1 H32 T8192 d128"] = roofline(
-            "mfma", f8["flop"], f8["median_ms"], "fa_fwd_fp8 causal B1 H32 T8192 d128", peak_tflops=PEAK_FP8_TFLOPS)
+        u = "fa_fwd_fp8 causal B1 H32 T8192 d128"
+        out["targets"][u] = roofline("mfma", f8["flop"], f8["median_ms"], u, peak_tflops=PEAK_FP8_TFLOPS)
         torch.cuda.empty_cache()
-        dr = run_attention("gpt2-medium-fwd-bwd", 20, 5, backward=True, p_drop=DROPOUT_P)
-        dr.pop("host")
+    if extras or want("dropout"):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(2)
+        w = W[2]
+        dev = {n: _randn_bf16((w.B, w.Hq, w.Tq, w.d), gen) for n in ("q", "k", "v", "do")}
+        _, t = timed(attention_calls(dev, False, True, DROPOUT_P, DROPOUT_SEED, DROPOUT_OFFSET), 20, 5, stream)
+        ff = fwd_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, False)
         out["targets"]["fa_fwd_dropout B64 H16 T1024 d64 p0.1"] = roofline(
-            "mfma", dr["fwd_flop"], dr["fwd_median_ms"], "fa_fwd_dropout B64 H16 T1024 d64 p0.1")
+            "mfma", ff, t["fwd"].median_ms(), "fa_fwd_dropout B64 H16 T1024 d64 p0.1")
         out["targets"]["fa_bwd_dropout B64 H16 T1024 d64 p0.1"] = roofline(
-            "mfma", dr["bwd_flop"], dr["bwd_median_ms"], "fa_bwd_dropout B64 H16 T1024 d64 p0.1",
-            bwd_algorithmic_bytes(B, Hq, Hkv, T, d))
-        f32 = run_small_f32(50, 10)
+            "mfma", 2.5 * ff, t["bwd"].median_ms(), "fa_bwd_dropout B64 H16 T1024 d64 p0.1",
+            bwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d))
+        del dev
+        torch.cuda.empty_cache()
+    if extras or want("f32"):
+        raw[1] = inputs.workload_inputs(W[1])
+        f32 = run_small_f32(raw[1], 50, 10)
         out["latency"] = {"fa_fwd_f32 B1 H1 T256 d64": {"median_us": round(f32["median_ms"] * 1e3, 2),
                                                         "flop": f32["flop"], "bound": "latency"}}
+    if args.only is not None and args.only != "headline":
+        print(json.dumps(out), flush=True)
+        return 0
+
+    # ---- headline: fa_fwd over the causal long-context layer
+    w = W[3]
+    dev = to_device(raw[3])
+    calls = attention_calls(dev, w.causal, False)
+    wall, t = timed(calls, args.steps, args.warmup, stream)
+    flop = fwd_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
+    ms_step = wall * 1e3 / args.steps
+    res = {
+        "metric": METRIC, "value": round(flop / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), the parity tests' inputs)",
+        "config": {"workload": "causal long-context attention forward (Llama-3-8B layer shape)", "B": w.B,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.Tq, "head_dim": w.d, "causal": True,
+                   "scale": w.scale, "step": "fa_fwd", "flop_per_step": flop,
+                   "flop_convention": "4*d per visible (query, key) pair; T(T+1)/2 causal pairs per head"},
+        # the step's only launch, fwd_bf16_kernel<128, true>
+        "roofline": roofline("mfma", flop, t["fwd"].mean_ms(), HEADLINE_UNIT,
+                             fwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d)),
+    }
+    res["roofline"]["median_ms"] = round(t["fwd"].median_ms(), 4)
+    if extras:
+        res["roofline"]["sclk_under_load"] = read_sclk_under_load(calls[0][1])
+        res["roofline"]["sclk_spec_mhz"] = SPEC_SCLK_MHZ
+    del dev
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+        for n in (1, 2, 4, 5):
+            if n not in raw:
+                raw[n] = inputs.workload_inputs(W[n])
+        res["cpu_baseline"] = cpu_baseline(raw, full=args.cpu_full)
+    res.update({k: v for k, v in out.items() if v})
+    print(json.dumps(res), flush=True)
     return 0
 
 
