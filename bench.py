@@ -733,8 +733,9 @@ def derived_counters(c):
         return d
     cyc = g / N_XCD                                   # busy clocks of one XCD
     if c.get("_duration_s"):
-        d["clock_mhz"] = round(cyc / c["_duration_s"] / 1e6)
         d["duration_us_under_counters"] = round(c["_duration_s"] * 1e6, 1)
+        if c["_duration_s"] >= 50e-6:   # shorter dispatches: launch overhead dominates the ratio
+            d["clock_mhz"] = round(cyc / c["_duration_s"] / 1e6)
     if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
         d["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD), 4)
         if c["SQ_VALU_MFMA_BUSY_CYCLES"] > 0 and "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
@@ -788,6 +789,35 @@ def record_counters(d):
     return 0
 
 
+def summarize_trace(d):
+    """Markdown table of the fa:: kernels in a rocprofv3 --kernel-trace run:
+    per (kernel, grid size) calls and durations, registers and LDS."""
+    paths = glob.glob(os.path.join(d, "*kernel_trace.csv"))
+    if not paths:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    rows = collections.defaultdict(list)
+    info = {}
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if not name.startswith("void fa::"):
+                continue
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            key = (kernel_key(name), grid)
+            rows[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            info[key] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"], r["Scratch_Size"],
+                         int(r["Workgroup_Size_X"]))
+    out = ["| kernel | grid (threads) | calls | avg us | min us | max us | VGPR | AGPR | LDS B | scratch B | block |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(rows, key=lambda k: -sum(rows[k])):
+        t = rows[key]
+        v, a, lds, scr, blk = info[key]
+        out.append(f"| `{key[0]}` | {key[1]} | {len(t)} | {np.mean(t):.1f} | {min(t):.1f} | {max(t):.1f} | {v} | {a} | "
+                   f"{lds} | {scr} | {blk} |")
+    print("\n".join(out))
+    return 0
+
+
 # ---------------------------------------------------------------------- main
 
 INPUT_WORKLOADS = None   # inputs.WORKLOADS, bound in main() (workers import it themselves)
@@ -804,6 +834,9 @@ def main():
                     help="oracle baseline with the GPT-2-medium layer in 3 passes and the 32k GQA layer's fwd+bwd "
                          "for KV groups 0 and 7 in full (minutes of CPU time)")
     ap.add_argument("--no-extras", action="store_true", help="headline only")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock reading (profiled runs: a profiler loaded into every child "
+                         "process makes starting amd-smi unsafe)")
     ap.add_argument("--only", choices=["headline", "step", "gqa32k", "decode", "dropout", "fp8", "window", "f32",
                                        "copy"],
                     help="run one measurement alone (profiling runs); 'copy' runs a plain device copy "
@@ -812,6 +845,8 @@ def main():
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
     ap.add_argument("--record-counters", metavar="DIR",
                     help="write profiles/counters.json from rocprofv3 --pmc passes in DIR/<pass>/ (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown table of the fa:: kernels of a rocprofv3 --kernel-trace run in DIR")
     ap.add_argument("--print-counter-passes", action="store_true",
                     help="print the counter passes, one comma-separated line each (for the profiling commands)")
     args = ap.parse_args()
@@ -819,6 +854,8 @@ def main():
         for p in COUNTER_PASSES:
             print(",".join(p))
         return 0
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
     if args.record_traffic:
         return record_traffic(args.record_traffic)
     if args.record_counters:
@@ -948,7 +985,7 @@ def main():
                              fwd_algorithmic_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.d)),
     }
     res["roofline"]["median_ms"] = round(t["fwd"].median_ms(), 4)
-    if extras:
+    if extras and not args.no_clock:
         res["roofline"]["sclk_under_load"] = read_sclk_under_load(calls[0][1])
         res["roofline"]["sclk_spec_mhz"] = SPEC_SCLK_MHZ
     del dev

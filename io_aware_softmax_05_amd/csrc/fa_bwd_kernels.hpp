@@ -157,13 +157,19 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   }
   const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
 
-  // Iteration order: query tiles from the last one down to the first that
-  // sees this workgroup's keys, and for each tile every query head of the
-  // group. The workgroups resident on one XCD hold consecutive key tiles of
-  // one KV head, so they start on the same (tile, head) and walk in step:
-  // each Q/dO tile they read is fetched once into that XCD's L2 instead of
-  // once per workgroup. Tile iterator for the loads (ahead of the compute):
-  int ld_it = 0, ld_h = 0, ld_qi = n_qt - 1;
+  // Iteration order. The workgroups resident on one XCD hold consecutive key
+  // tiles of one KV head.
+  //   * Without a window: query tiles from the last one down to the first
+  //     that sees this workgroup's keys, every query head of the group per
+  //     tile. The resident workgroups start on the same (tile, head) and walk
+  //     in step, so each Q/dO tile they read is fetched once into the XCD's L2.
+  //   * With a window each workgroup sees only a band of about W / BQ tiles
+  //     that starts at its diagonal: the heads are outermost and the tiles go
+  //     up from the diagonal, so a neighbour reads the same tile two steps
+  //     later, while it is still in L2.
+  // DOWN is the first order. Tile iterator for the loads (ahead of the compute):
+  constexpr bool DOWN = !WIN;
+  int ld_it = 0, ld_h = 0, ld_qi = DOWN ? n_qt - 1 : qt_begin;
   // Rows past Tq lie past the end of the buffer ranges and read as zeros, so
   // only an exhausted iterator needs an out-of-range base.
   auto issue = [&](auto stage_c) FA_INLINE {
@@ -186,9 +192,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
       dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE), sbase + (uint32_t)row * 4);
     }
     ++ld_it;
-    if (++ld_h == G) {
-      ld_h = 0;
-      if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
+    if constexpr (DOWN) {
+      if (++ld_h == G) {
+        ld_h = 0;
+        if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
+      }
+    } else if (++ld_qi == n_qt) {
+      ld_qi = qt_begin;
+      if (ld_h + 1 < G) ++ld_h;          // past the last head: loads read zeros (live is false)
     }
   };
 
@@ -316,26 +327,41 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
     static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(st); });
     wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
   }
-  int cur_qi = n_qt - 1, cur_h = 0;
-  auto step = [&](auto stage_c) FA_INLINE {
+  int cur_qi = DOWN ? n_qt - 1 : qt_begin, cur_h = 0;
+  auto step = [&](auto stage_c, auto may_mask) FA_INLINE {
     constexpr int CS = decltype(stage_c)::value;
     issue(std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});   // zeros past the end
     const FA_LDS uint8_t* st = smem + CS * STAGE;
     const int q0 = cur_qi * BQ;
     // some (row, key) pair of this wave is masked (causal limit or window start)
-    if ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0))
+    if (decltype(may_mask)::value &&
+        ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0)))
       body(st, q0, cur_h, std::true_type{});
     else
       body(st, q0, cur_h, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();          // the next tile has landed; this stage is free
-    if (++cur_h == G) {
-      cur_h = 0;
-      --cur_qi;
+    if constexpr (DOWN) {
+      if (++cur_h == G) {
+        cur_h = 0;
+        --cur_qi;
+      }
+    } else if (++cur_qi == n_qt) {
+      cur_qi = qt_begin;
+      ++cur_h;
     }
   };
-  for (int it = 0; it < n_iter; it += C::NSTAGE)
+  int it = 0;
+  if constexpr (CAUSAL && !WIN) {
+    // tiles whose first row sees every key of the workgroup need no mask; the
+    // downward walk visits them first (whole groups of NSTAGE iterations)
+    const int qi_full = (k0 + C::BK - 1 - shift + BQ - 1) / BQ;   // first tile with no masked pair
+    const int it_full = max(0, n_qt - max(qi_full, qt_begin)) * G / C::NSTAGE * C::NSTAGE;
+    for (; it < it_full; it += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(s, std::false_type{}); });
+  }
+  for (; it < n_iter; it += C::NSTAGE)
     static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
-      if (it + decltype(s)::value < n_iter) step(s);
+      if (it + decltype(s)::value < n_iter) step(s, std::true_type{});
     });
   if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
@@ -366,8 +392,8 @@ namespace {
 // CU) and 32-key tiles; d = 128: 4 waves with up to 512 registers each (8
 // waves spill), 64-key tiles and the MFMA/exp interleave hint. Both measured
 // fastest on MI355X.
-template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = (D == 64 ? 32 : 64), int NSTAGE_ = (D == 64 ? 2 : 3),
-          int IGLP_ = (D == 64 ? -1 : 2), int OCC_ = 1>
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = (D == 64 ? 32 : 32), int NSTAGE_ = (D == 64 ? 2 : 3),
+          int IGLP_ = (D == 64 ? -1 : 2), int OCC_ = (D == 64 ? 1 : 2)>
 struct DqCfg {
   static constexpr int NW = NW_;                      // waves per workgroup
   static constexpr int OCC = OCC_;                    // workgroups per CU the register budget allows
@@ -596,20 +622,30 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(j_begin + decltype(st)::value, st); });
     wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
   }
-  auto step = [&](int j, auto stage_c) FA_INLINE {
+  auto step = [&](int j, auto stage_c, auto may_mask) FA_INLINE {
     constexpr int CS = decltype(stage_c)::value;
     issue(j + C::NSTAGE - 1, std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});
     const FA_LDS uint8_t* st = smem + CS * STAGE;
     // some (row, key) pair of this wave is masked (causal limit or window start)
-    if ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1))
+    if (decltype(may_mask)::value &&
+        ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1)))
       body(st, j, std::true_type{});
     else
       body(st, j, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();
   };
-  for (int j = j_begin; j < n_kv; j += C::NSTAGE)
+  int j = j_begin;
+  if constexpr (CAUSAL && !WIN) {
+    // key tiles every row of the workgroup sees whole need no mask; they come
+    // first (whole groups of NSTAGE tiles), in a loop of their own, so the
+    // masked body's registers do not weigh on it
+    const int j_full = j_begin + (min(n_kv, max(0, q0 + shift + 1) / BC) - j_begin) / C::NSTAGE * C::NSTAGE;
+    for (; j < j_full; j += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(j + decltype(s)::value, s, std::false_type{}); });
+  }
+  for (; j < n_kv; j += C::NSTAGE)
     static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
-      if (j + decltype(s)::value < n_kv) step(j + decltype(s)::value, s);
+      if (j + decltype(s)::value < n_kv) step(j + decltype(s)::value, s, std::true_type{});
     });
   if (j_begin < n_kv) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
 
