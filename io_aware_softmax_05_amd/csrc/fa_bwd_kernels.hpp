@@ -389,10 +389,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 namespace {
 
 // d = 64: 8 waves (two per SIMD at about 128 registers, so two workgroups per
-// CU) and 32-key tiles; d = 128: 4 waves with up to 512 registers each (8
-// waves spill), 64-key tiles and the MFMA/exp interleave hint. Both measured
-// fastest on MI355X.
-template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = (D == 64 ? 32 : 32), int NSTAGE_ = (D == 64 ? 2 : 3),
+// CU) and 32-key tiles; d = 128: 4 waves, 32-key tiles in a 3-stage ring and
+// two workgroups per CU (256 registers per wave), with the MFMA/exp interleave
+// hint. Both measured fastest on MI355X (at d = 128 the causal loop must be
+// split, see bwd_dq_kernel, for the two-workgroup tiling to fit).
+template <int D, int NW_ = (D == 64 ? 8 : 4), int BC_ = 32, int NSTAGE_ = (D == 64 ? 2 : 3),
           int IGLP_ = (D == 64 ? -1 : 2), int OCC_ = (D == 64 ? 1 : 2)>
 struct DqCfg {
   static constexpr int NW = NW_;                      // waves per workgroup
@@ -669,9 +670,18 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 // check that the result does not depend on the tile shape: dQ takes 64-key
 // tiles where the default takes 32 and 32 where it takes 64, dK/dV walks
 // 32-row query tiles where the default walks 64 and 64 where it walks 32.
+// One workgroup per CU with 64-key tiles at d = 128, for the dQ passes whose
+// registers do not fit the two-workgroup tiling: the sliding window (it masks
+// tiles at both ends of a row's key range, so its loop is not split; the
+// two-workgroup tiling spills there and measured 1.8x slower) and dropout
+// (the Philox bytes of a tile).
+template <int D>
+using DqOneCfg = DqCfg<D, DqCfg<D>::NW, (D == 64 ? 32 : 64), (D == 64 ? 2 : 3), DqCfg<D>::IGLP, 1>;
+
 template <int D, bool CAUSAL, bool WIN = false, bool DROP = false, bool ALT = false>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
-  using QC = typename std::conditional<ALT, DqCfg<D, DqCfg<D>::NW, (DqCfg<D>::BC == 32 ? 64 : 32)>, DqCfg<D>>::type;
+  using QD = typename std::conditional<WIN || DROP, DqOneCfg<D>, DqCfg<D>>::type;
+  using QC = typename std::conditional<ALT, DqCfg<D, QD::NW, (QD::BC == 32 ? 64 : 32)>, QD>::type;
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + QC::BR - 1) / QC::BR;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QC, WIN, DROP>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(QC::NT), 0,
