@@ -90,7 +90,7 @@ TRAFFIC_UNITS = {
     "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128, 3>", "decode_merge_kernel<128>"],
     "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false, false>@2097152"],
     "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false, false>",
-                                                   "bwd_dkdv_kernel<128, true, false, false>"],
+                                                   "bwd_dkdv16_kernel<128, true>"],
     "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true, false>"],
     "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["bwd_dq_kernel<128, true, true, false>",
                                                      "bwd_dkdv_kernel<128, true, true, false>"],
@@ -109,7 +109,7 @@ def fwd_flops(B, Hq, Tq, Tk, d, causal):
 # Source file of each kernel family; every kernel also depends on the shared headers.
 _BWD = ("fa_bwd_kernels.hpp", "fa_bwd.hip", "fa_bwd_window.hip")
 KERNEL_SOURCES = {"fwd_bf16_kernel": ("fa_fwd.hip",), "fwd_fp8_kernel": ("fa_fwd_fp8.hip",),
-                  "bwd_dq_kernel": _BWD, "bwd_dkdv_kernel": _BWD,
+                  "bwd_dq_kernel": _BWD, "bwd_dkdv_kernel": _BWD, "bwd_dkdv16_kernel": _BWD,
                   "decode_split_kernel": ("fa_decode.hip",), "decode_merge_kernel": ("fa_decode.hip",)}
 SHARED_SOURCES = ("fa_common.hpp", "fa_internal.h")
 

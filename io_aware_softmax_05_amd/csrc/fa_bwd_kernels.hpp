@@ -384,6 +384,270 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   }
 }
 
+// ------------------------------------------------- dk dv, 16 keys per wave
+
+namespace {
+
+// d = 128 without window or dropout: 8 waves of 16 keys each (128 keys per
+// workgroup) on v_mfma_f32_16x16x32_bf16. Each wave holds half the state of
+// the 32-key layout (K and V fragments, dK and dV accumulators, S and dP of
+// one query tile), about 150 registers instead of up to 512, so two waves
+// share every SIMD and hide each other's LDS and barrier waits. The price is
+// twice the LDS operand reads per MFMA: every Q or dO fragment now serves 16
+// keys instead of 32.
+template <int D, int NSTAGE_ = 3>
+struct Dkdv16Cfg {
+  static constexpr int NW = 8;                       // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int BK = 16 * NW;                 // keys per workgroup
+  static constexpr int BQ = 64;                      // query rows per tile
+  static constexpr int RB = BQ / 16;                 // 16-row blocks per tile
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CH = D / 8;
+  static constexpr int QTILE = BQ * ROWB;
+  static constexpr int SLOT = (BQ * 4 + 255) / 256 * 256;
+  static constexpr int STATS = 2 * SLOT;
+  static constexpr int STAGE = 2 * QTILE + STATS;
+  static constexpr int NSTAGE = NSTAGE_;
+  static constexpr int TILE_DMA = 2 * BQ * CH / 64;
+  static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
+  static constexpr int STAT_DMA = STATS / 256;
+  static constexpr int VM_PER_TILE = DMA_PER_WAVE + STAT_DMA;
+  static_assert(D == 128, "the 16-key layout is built for d = 128");
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
+};
+
+// Chunk swizzle of this kernel's Q and dO tiles (rows of 256 bytes, one bank
+// row each): chunk c of row r lives at chunk c ^ swz16(r). Measured on gfx950
+// with the LDS bank-conflict counter, ds_read_b128 serves a wave in four
+// passes of 16 lanes, told apart by lane bit 5 and by the parity of lane bits
+// 2, 3 and 4, and ds_read_b64_tr_b16 in two passes (lanes 0-31, 32-63). With
+// this table both read patterns of the kernel give every lane of a pass its
+// own banks: the A-operand reads (16 rows at chunks 4 ks + q) and the
+// transposed reads (8 consecutive rows at two neighbouring chunks). The 32x32
+// kernels' swizzle leaves 2-way conflicts on both here.
+__device__ __forceinline__ uint32_t swz16(uint32_t r) {
+  return (((r & 7u) << 1) | ((r >> 3) & 1u)) ^ (r & 8u);
+}
+
+}  // namespace
+
+// One workgroup per 128 keys of one KV head; wave w owns keys k0 + 16 w ..
+// k0 + 16 w + 15, lane (q = lane / 16, c = lane % 16) key k0 + 16 w + c.
+//   S = Q K^T, dP = dO V^T   per 16-row block: lane holds rows 4 q .. 4 q + 3
+//   dV^T += dO^T P, dK^T += Q^T dS   per 32-row step; k-slot (q, e) of the
+//       step is row 4 q + e (e < 4) or 16 + 4 q + e - 4 (e >= 4), so P and dS
+//       go from the S/dP accumulators into the B operand with no lane
+//       exchange, and the A operand (dO^T or Q^T) comes from two transposed
+//       LDS reads of 4 consecutive rows each.
+// The query tiles are walked as in bwd_dkdv_kernel without a window: from the
+// last tile down, every query head of the group per tile.
+template <int D, bool CAUSAL, class C = Dkdv16Cfg<D>>
+__global__ __launch_bounds__(C::NT, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_ktiles) {
+  constexpr int BQ = C::BQ, RB = C::RB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
+  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, col = lane & 15;
+
+  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = (int)(t % (uint32_t)n_ktiles);   // causal: small kt has the most work
+  const int bhk = (int)(t / (uint32_t)n_ktiles);
+  const int b = bhk / a.Hkv, hk = bhk - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + wave * 16;                 // first key of this wave
+  const int key = kw0 + col;                      // this lane's key
+  const int shift = a.Tk - a.Tq;
+  const size_t kvoff = (size_t)bhk * a.Tk * D;
+
+  // B operands: lane (q, c) holds K[key][32 ks + 8 q + e] and V[key][...], e < 8.
+  bf16x8 kf[D / 32], vf[D / 32];
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+    const uint32_t base = key < a.Tk ? (uint32_t)(key * D + 8 * q) * 2 : kOutOfRange;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      kf[ks] = as_bf16x8(buf_load_b128(krs, base + ks * 64));
+      vf[ks] = as_bf16x8(buf_load_b128(vrs, base + ks * 64));
+    }
+  }
+
+  // dV^T and dK^T in 16-wide d blocks: register r of block db is d = 16 db + 4 q + r.
+  f32x4 dv_acc[D / 16], dk_acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    dv_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dk_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  int qt_begin = 0;
+  if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
+  const int n_qt = (a.Tq + BQ - 1) / BQ;
+  const int per_head = max(0, n_qt - qt_begin);
+  const int n_iter = per_head * G;
+
+  // This thread's share of the tile loads (physical chunk p of a row holds
+  // logical chunk p ^ swz16(row)).
+  uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+  bool dma_is_do[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int n = wave * C::DMA_PER_WAVE + i;
+    const int m = n % (C::TILE_DMA / 2);
+    dma_is_do[i] = n >= C::TILE_DMA / 2;
+    const int p = 64 * m + lane;
+    const int r = p / CH, pc = p % CH;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz16(r)) * 8) * 2;
+    dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
+  }
+  const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
+
+  int ld_it = 0, ld_h = 0, ld_qi = n_qt - 1;
+  auto issue = [&](auto stage_c) FA_INLINE {
+    FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
+    const bool live = ld_it < n_iter;
+    const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.stats + rows, (uint32_t)a.Tq * 4);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.stats + plane + rows, (uint32_t)a.Tq * 4);
+    const uint32_t tbase = live ? (uint32_t)(ld_qi * BQ) * D * 2 : kOutOfRange;
+    const uint32_t sbase = live ? (uint32_t)(ld_qi * BQ) * 4 : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], tbase + dma_off[i]);
+#pragma unroll
+    for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
+      constexpr int PER_PLANE = C::STAT_DMA / 2;
+      const int pl = i / PER_PLANE, row = 64 * (i % PER_PLANE) + lane;
+      dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE), sbase + (uint32_t)row * 4);
+    }
+    ++ld_it;
+    if (++ld_h == G) {
+      ld_h = 0;
+      if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
+    }
+  };
+
+  // LDS read offsets inside a tile. A operand of S and dP: row 16 rb + c,
+  // logical chunk 4 ks + q (^ 64 ks on the byte offset).
+  const uint32_t a_rd = col * ROWB + 16 * (q ^ swz16(col));
+  // Transposed reads: lane c of group q names row 4 q + c / 4 of a 16-row
+  // block and the 8 bytes at d = 16 db + 4 (c % 4) (^ 32 db on the offset).
+  const uint32_t tr_row = 4 * q + (col >> 2);
+  const uint32_t tr_rd = tr_row * ROWB + 16 * (((col & 3) >> 1) ^ swz16(tr_row)) + 8 * (col & 1);
+
+  auto body = [&](const FA_LDS uint8_t* st, int q0, auto masked) FA_INLINE {
+    const FA_LDS uint8_t* qt = st;
+    const FA_LDS uint8_t* gt = st + QTILE;
+    const FA_LDS uint8_t* stt = st + 2 * QTILE;
+    // Unmasked tiles start the dP product from -D of the lane's four rows.
+    constexpr bool FOLD = !decltype(masked)::value;
+    f32x4 s[RB], dp[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x4 dinit{};
+      if constexpr (FOLD) dinit = *(const FA_LDS f32x4*)(stt + C::SLOT + (16 * rb + 4 * q) * 4);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const uint32_t off = rb * 16 * ROWB + (a_rd ^ (64 * ks));
+        s[rb] = mfma16(as_bf16x8(lds_read_b128(qt, off)), kf[ks], ks == 0 ? f32x4{} : s[rb]);
+        dp[rb] = mfma16(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? dinit : dp[rb]);
+      }
+    }
+    // P and dS of rows 16 rb + 4 q + e, packed in pairs; masked tiles: row
+    // q0 + 16 rb + 4 q + e sees this lane's key iff dbase + 16 rb + e >= 0.
+    const int dbase = q0 + 4 * q + shift - key;
+    uint32_t pw[RB][2], dsw[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4 l2 = *(const FA_LDS f32x4*)(stt + (16 * rb + 4 * q) * 4);
+      f32x4 nd{};
+      if constexpr (!FOLD) nd = *(const FA_LDS f32x4*)(stt + C::SLOT + (16 * rb + 4 * q) * 4);
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pe = exp2_fast(fmaf(s[rb][e], a.c, -l2[e]));
+        if constexpr (decltype(masked)::value) {
+          if (dbase + 16 * rb + e < 0) pe = 0.f;
+        }
+        p[e] = pe;
+        ds[e] = pe * (FOLD ? dp[rb][e] : dp[rb][e] + nd[e]);
+      }
+      pw[rb][0] = pack_bf16x2(p[0], p[1]);
+      pw[rb][1] = pack_bf16x2(p[2], p[3]);
+      dsw[rb][0] = pack_bf16x2(ds[0], ds[1]);
+      dsw[rb][1] = pack_bf16x2(ds[2], ds[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, 32 rows (blocks 2 hs and 2 hs + 1) per step.
+#pragma unroll
+    for (int hs = 0; hs < BQ / 32; ++hs) {
+      const bf16x8 pb = as_bf16x8(u32x4{pw[2 * hs][0], pw[2 * hs][1], pw[2 * hs + 1][0], pw[2 * hs + 1][1]});
+      const bf16x8 sb = as_bf16x8(u32x4{dsw[2 * hs][0], dsw[2 * hs][1], dsw[2 * hs + 1][0], dsw[2 * hs + 1][1]});
+      const uint32_t lo = 32 * hs * ROWB, hi = (32 * hs + 16) * ROWB;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint32_t o = tr_rd ^ (32 * db);
+        const u32x2 glo = lds_read_tr(gt, lo + o), ghi = lds_read_tr(gt, hi + o);
+        dv_acc[db] = mfma16(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
+        const u32x2 qlo = lds_read_tr(qt, lo + o), qhi = lds_read_tr(qt, hi + o);
+        dk_acc[db] = mfma16(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+      }
+    }
+  };
+
+  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::VM_PER_TILE;
+  if (n_iter > 0) {
+    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(st); });
+    wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
+  }
+  int cur_qi = n_qt - 1, cur_h = 0;
+  auto step = [&](auto stage_c, auto may_mask) FA_INLINE {
+    constexpr int CS = decltype(stage_c)::value;
+    issue(std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});   // zeros past the end
+    const FA_LDS uint8_t* st = smem + CS * STAGE;
+    const int q0 = cur_qi * BQ;
+    if (decltype(may_mask)::value && CAUSAL && q0 + shift < kw0 + 15)   // some pair of this wave is masked
+      body(st, q0, std::true_type{});
+    else
+      body(st, q0, std::false_type{});
+    wait_vm_barrier<AHEAD_VM>();          // the next tile has landed; this stage is free
+    if (++cur_h == G) {
+      cur_h = 0;
+      --cur_qi;
+    }
+  };
+  int it = 0;
+  if constexpr (CAUSAL) {
+    // tiles whose first row sees every key of the workgroup need no mask; the
+    // walk visits them first (whole groups of NSTAGE iterations)
+    const int qi_full = (k0 + C::BK - 1 - shift + BQ - 1) / BQ;
+    const int it_full = max(0, n_qt - max(qi_full, qt_begin)) * G / C::NSTAGE * C::NSTAGE;
+    for (; it < it_full; it += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(s, std::false_type{}); });
+  }
+  for (; it < n_iter; it += C::NSTAGE)
+    static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+      if (it + decltype(s)::value < n_iter) step(s, std::true_type{});
+    });
+  if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
+
+  if (key < a.Tk) {
+    uint16_t* dkp = a.dk + kvoff + (size_t)key * D + 4 * q;
+    uint16_t* dvp = a.dv + kvoff + (size_t)key * D + 4 * q;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const f32x4 kk = dk_acc[db], vv = dv_acc[db];
+      *(u32x2*)(dkp + 16 * db) = u32x2{pack_bf16x2(kk[0] * a.scale, kk[1] * a.scale),
+                                       pack_bf16x2(kk[2] * a.scale, kk[3] * a.scale)};
+      *(u32x2*)(dvp + 16 * db) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+    }
+  }
+}
+
 // -------------------------------------------------------------------- dq
 
 namespace {
@@ -694,6 +958,13 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   // 64-row masked body past 512 registers)
   using KD = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
              typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>, DkdvCfg<D>>::type>::type;
+  if constexpr (D == 128 && !WIN && !DROP && !ALT) {   // two waves per SIMD (16 keys per wave)
+    using K16 = Dkdv16Cfg<D>;
+    const int n_ktiles = (a.Tk + K16::BK - 1) / K16::BK;
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, K16>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(K16::NT), 0,
+                       stream, a, n_ktiles);
+    return hipGetLastError();
+  }
   using KC = typename std::conditional<ALT, DkdvCfg<D, KD::NW, (KD::BQ == 64 ? 32 : 64)>, KD>::type;
   const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0,
