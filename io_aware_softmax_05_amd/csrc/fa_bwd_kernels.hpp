@@ -582,6 +582,10 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_k
       dsw[rb][0] = pack_bf16x2(ds[0], ds[1]);
       dsw[rb][1] = pack_bf16x2(ds[2], ds[3]);
     }
+    // The compiler's interleave strategy 1 on the causal unmasked body
+    // (measured on MI355X: causal 32k GQA backward -4.5%; the non-causal
+    // instantiation ran 23% slower with it and takes none).
+    if constexpr (CAUSAL && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(1);
     // dV^T += dO^T P and dK^T += Q^T dS, 32 rows (blocks 2 hs and 2 hs + 1) per step.
 #pragma unroll
     for (int hs = 0; hs < BQ / 32; ++hs) {
