@@ -24,11 +24,15 @@
 //         transposed LDS reads. Its prologue also forms each row's
 //         D_i = rowsum(dO * O) and LSE * log2(e) and stores them for dkdv
 //         (two planes: LSE * log2(e) of every row, then -D).
-//   dkdv  one workgroup per 32 keys per wave of a KV head (K and V
+//   dkdv  one workgroup per 16 or 32 keys per wave of a KV head (K and V
 //         fragments held in registers); it walks every query tile of every
 //         query head of the group. S = Q K^T puts one key per lane, so P and
 //         dS feed dV^T = dO^T P and dK^T = Q^T dS straight from the
 //         accumulators; dO^T and Q^T come from ds_read_b64_tr_b16.
+//         bwd_dkdv16_kernel (16 keys per wave on 16x16x32 MFMAs, two or four
+//         waves per SIMD) serves d = 128 and causal d = 64; bwd_dkdv_kernel
+//         (32 keys per wave on 32x32x16 MFMAs) the sliding window, dropout,
+//         non-causal d = 64 and the second tiling.
 #pragma once
 #include <type_traits>
 
@@ -388,16 +392,17 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 
 namespace {
 
-// d = 128 without window or dropout: 8 waves of 16 keys each (128 keys per
+// Without window or dropout: 8 waves of 16 keys each (128 keys per
 // workgroup) on v_mfma_f32_16x16x32_bf16. Each wave holds half the state of
 // the 32-key layout (K and V fragments, dK and dV accumulators, S and dP of
 // one query tile), about 150 registers instead of up to 512, so two waves
 // share every SIMD and hide each other's LDS and barrier waits. The price is
 // twice the LDS operand reads per MFMA: every Q or dO fragment now serves 16
 // keys instead of 32.
-template <int D, int NSTAGE_ = 3>
+template <int D, int NSTAGE_ = (D == 64 ? 2 : 3)>
 struct Dkdv16Cfg {
   static constexpr int NW = 8;                       // waves per workgroup
+  static constexpr int OCC = D == 64 ? 2 : 1;        // workgroups per CU the register budget allows
   static constexpr int NT = 64 * NW;
   static constexpr int BK = 16 * NW;                 // keys per workgroup
   static constexpr int BQ = 64;                      // query rows per tile
@@ -413,21 +418,27 @@ struct Dkdv16Cfg {
   static constexpr int DMA_PER_WAVE = TILE_DMA / NW;
   static constexpr int STAT_DMA = STATS / 256;
   static constexpr int VM_PER_TILE = DMA_PER_WAVE + STAT_DMA;
-  static_assert(D == 128, "the 16-key layout is built for d = 128");
+  static_assert(D == 64 || D == 128, "head width");
   static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW == TILE_DMA, "tile loads must split over the waves");
 };
 
-// Chunk swizzle of this kernel's Q and dO tiles (rows of 256 bytes, one bank
-// row each): chunk c of row r lives at chunk c ^ swz16(r). Measured on gfx950
-// with the LDS bank-conflict counter, ds_read_b128 serves a wave in four
-// passes of 16 lanes, told apart by lane bit 5 and by the parity of lane bits
-// 2, 3 and 4, and ds_read_b64_tr_b16 in two passes (lanes 0-31, 32-63). With
-// this table both read patterns of the kernel give every lane of a pass its
-// own banks: the A-operand reads (16 rows at chunks 4 ks + q) and the
-// transposed reads (8 consecutive rows at two neighbouring chunks). The 32x32
-// kernels' swizzle leaves 2-way conflicts on both here.
+// Chunk swizzle of this kernel's Q and dO tiles: chunk c of row r lives at
+// chunk c ^ swz16<D>(r). Measured on gfx950 with the LDS bank-conflict
+// counter, ds_read_b128 serves a wave in four passes of 16 lanes, told apart
+// by lane bit 5 and by the parity of lane bits 2, 3 and 4, and
+// ds_read_b64_tr_b16 in two passes (lanes 0-31, 32-63). These tables give
+// every lane of a pass its own banks in both read patterns of the kernel: the
+// A-operand reads (16 rows at chunks 4 ks + q) and the transposed reads (8
+// consecutive rows at two neighbouring chunks). At d = 128 a row is one bank
+// row; at d = 64 two rows share one, so the table ignores row bit 0. The
+// 32x32 kernels' swizzles leave 2-way conflicts on both patterns here.
+template <int D>
 __device__ __forceinline__ uint32_t swz16(uint32_t r) {
-  return (((r & 7u) << 1) | ((r >> 3) & 1u)) ^ (r & 8u);
+  if constexpr (D == 128) {
+    return (((r & 7u) << 1) | ((r >> 3) & 1u)) ^ (r & 8u);
+  } else {
+    return (((r >> 1) & 3u) << 1) ^ (((r >> 3) & 1u) * 5u);
+  }
 }
 
 }  // namespace
@@ -443,7 +454,7 @@ __device__ __forceinline__ uint32_t swz16(uint32_t r) {
 // The query tiles are walked as in bwd_dkdv_kernel without a window: from the
 // last tile down, every query head of the group per tile.
 template <int D, bool CAUSAL, class C = Dkdv16Cfg<D>>
-__global__ __launch_bounds__(C::NT, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_ktiles) {
+__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, int n_ktiles) {
   constexpr int BQ = C::BQ, RB = C::RB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_k
   const int n_iter = per_head * G;
 
   // This thread's share of the tile loads (physical chunk p of a row holds
-  // logical chunk p ^ swz16(row)).
+  // logical chunk p ^ swz16<D>(row)).
   uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
   bool dma_is_do[C::DMA_PER_WAVE];
 #pragma unroll
@@ -501,7 +512,7 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_k
     dma_is_do[i] = n >= C::TILE_DMA / 2;
     const int p = 64 * m + lane;
     const int r = p / CH, pc = p % CH;
-    dma_off[i] = (uint32_t)(r * D + (pc ^ swz16(r)) * 8) * 2;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz16<D>(r)) * 8) * 2;
     dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
   }
   const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
@@ -534,11 +545,11 @@ __global__ __launch_bounds__(C::NT, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_k
 
   // LDS read offsets inside a tile. A operand of S and dP: row 16 rb + c,
   // logical chunk 4 ks + q (^ 64 ks on the byte offset).
-  const uint32_t a_rd = col * ROWB + 16 * (q ^ swz16(col));
+  const uint32_t a_rd = col * ROWB + 16 * (q ^ swz16<D>(col));
   // Transposed reads: lane c of group q names row 4 q + c / 4 of a 16-row
   // block and the 8 bytes at d = 16 db + 4 (c % 4) (^ 32 db on the offset).
   const uint32_t tr_row = 4 * q + (col >> 2);
-  const uint32_t tr_rd = tr_row * ROWB + 16 * (((col & 3) >> 1) ^ swz16(tr_row)) + 8 * (col & 1);
+  const uint32_t tr_rd = tr_row * ROWB + 16 * (((col & 3) >> 1) ^ swz16<D>(tr_row)) + 8 * (col & 1);
 
   auto body = [&](const FA_LDS uint8_t* st, int q0, auto masked) FA_INLINE {
     const FA_LDS uint8_t* qt = st;
@@ -962,7 +973,11 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   // 64-row masked body past 512 registers)
   using KD = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
              typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>, DkdvCfg<D>>::type>::type;
-  if constexpr (D == 128 && !WIN && !DROP && !ALT) {   // two waves per SIMD (16 keys per wave)
+  // 16 keys per wave at d = 128, and for causal d = 64 (measured on MI355X:
+  // causal GQA 32k backward -6%, causal B64 H16 T1024 d64 -20%; the
+  // non-causal d = 64 layer timed the same with either layout and keeps the
+  // 32-key one)
+  if constexpr (!WIN && !DROP && !ALT && (D == 128 || CAUSAL)) {
     using K16 = Dkdv16Cfg<D>;
     const int n_ktiles = (a.Tk + K16::BK - 1) / K16::BK;
     hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, K16>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(K16::NT), 0,
