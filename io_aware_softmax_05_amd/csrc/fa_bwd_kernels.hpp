@@ -30,9 +30,9 @@
 //         dS feed dV^T = dO^T P and dK^T = Q^T dS straight from the
 //         accumulators; dO^T and Q^T come from ds_read_b64_tr_b16.
 //         bwd_dkdv16_kernel (16 keys per wave on 16x16x32 MFMAs, two or four
-//         waves per SIMD) serves d = 128 and causal d = 64; bwd_dkdv_kernel
-//         (32 keys per wave on 32x32x16 MFMAs) the sliding window, dropout,
-//         non-causal d = 64 and the second tiling.
+//         waves per SIMD) serves d = 128 and causal d = 64, with or without a
+//         window; bwd_dkdv_kernel (32 keys per wave on 32x32x16 MFMAs)
+//         dropout, non-causal d = 64 and the second tiling.
 #pragma once
 #include <type_traits>
 
@@ -392,8 +392,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
 
 namespace {
 
-// Without window or dropout: 8 waves of 16 keys each (128 keys per
-// workgroup) on v_mfma_f32_16x16x32_bf16. Each wave holds half the state of
+// Without dropout: 8 waves of 16 keys each (128 keys per workgroup) on
+// v_mfma_f32_16x16x32_bf16. Each wave holds half the state of
 // the 32-key layout (K and V fragments, dK and dV accumulators, S and dP of
 // one query tile), about 150 registers instead of up to 512, so two waves
 // share every SIMD and hide each other's LDS and barrier waits. The price is
@@ -453,8 +453,9 @@ __device__ __forceinline__ uint32_t swz16(uint32_t r) {
 //       LDS reads of 4 consecutive rows each.
 // The query tiles are walked as in bwd_dkdv_kernel without a window: from the
 // last tile down, every query head of the group per tile.
-template <int D, bool CAUSAL, class C = Dkdv16Cfg<D>>
+template <int D, bool CAUSAL, class C = Dkdv16Cfg<D>, bool WIN = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, int n_ktiles) {
+  static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   constexpr int BQ = C::BQ, RB = C::RB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
@@ -497,7 +498,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
 
   int qt_begin = 0;
   if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
-  const int n_qt = (a.Tq + BQ - 1) / BQ;
+  int n_qt = (a.Tq + BQ - 1) / BQ;
+  if (WIN) {   // rows past the last key's window see none of these keys
+    const int last_row = k0 + C::BK - 1 - shift + a.window - 1;
+    n_qt = last_row < 0 ? 0 : min(n_qt, last_row / BQ + 1);
+  }
   const int per_head = max(0, n_qt - qt_begin);
   const int n_iter = per_head * G;
 
@@ -517,7 +522,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
   }
   const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
 
-  int ld_it = 0, ld_h = 0, ld_qi = n_qt - 1;
+  // Walk order as in bwd_dkdv_kernel: without a window from the last query
+  // tile down, the group's heads innermost; with one the heads outermost and
+  // the tiles up from the workgroup's diagonal.
+  constexpr bool DOWN = !WIN;
+  int ld_it = 0, ld_h = 0, ld_qi = DOWN ? n_qt - 1 : qt_begin;
   auto issue = [&](auto stage_c) FA_INLINE {
     FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
     const bool live = ld_it < n_iter;
@@ -537,9 +546,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
       dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE), sbase + (uint32_t)row * 4);
     }
     ++ld_it;
-    if (++ld_h == G) {
-      ld_h = 0;
-      if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
+    if constexpr (DOWN) {
+      if (++ld_h == G) {
+        ld_h = 0;
+        if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
+      }
+    } else if (++ld_qi == n_qt) {
+      ld_qi = qt_begin;
+      if (ld_h + 1 < G) ++ld_h;          // past the last head: loads read zeros (live is false)
     }
   };
 
@@ -570,7 +584,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
       }
     }
     // P and dS of rows 16 rb + 4 q + e, packed in pairs; masked tiles: row
-    // q0 + 16 rb + 4 q + e sees this lane's key iff dbase + 16 rb + e >= 0.
+    // q0 + 16 rb + 4 q + e sees this lane's key iff 0 <= dist < window with
+    // dist = dbase + 16 rb + e (no upper limit without a window).
     const int dbase = q0 + 4 * q + shift - key;
     uint32_t pw[RB][2], dsw[RB][2];
 #pragma unroll
@@ -583,7 +598,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
       for (int e = 0; e < 4; ++e) {
         float pe = exp2_fast(fmaf(s[rb][e], a.c, -l2[e]));
         if constexpr (decltype(masked)::value) {
-          if (dbase + 16 * rb + e < 0) pe = 0.f;
+          const int dist = dbase + 16 * rb + e;   // one unsigned compare for the band
+          if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
         }
         p[e] = pe;
         ds[e] = pe * (FOLD ? dp[rb][e] : dp[rb][e] + nd[e]);
@@ -596,7 +612,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
     // The compiler's interleave strategy 1 on the causal unmasked body
     // (measured on MI355X: causal 32k GQA backward -4.5%; the non-causal
     // instantiation ran 23% slower with it and takes none).
-    if constexpr (CAUSAL && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(1);
+    if constexpr (CAUSAL && !WIN && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(1);
     // dV^T += dO^T P and dK^T += Q^T dS, 32 rows (blocks 2 hs and 2 hs + 1) per step.
 #pragma unroll
     for (int hs = 0; hs < BQ / 32; ++hs) {
@@ -619,24 +635,31 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
     static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(st); });
     wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
   }
-  int cur_qi = n_qt - 1, cur_h = 0;
+  int cur_qi = DOWN ? n_qt - 1 : qt_begin, cur_h = 0;
   auto step = [&](auto stage_c, auto may_mask) FA_INLINE {
     constexpr int CS = decltype(stage_c)::value;
     issue(std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});   // zeros past the end
     const FA_LDS uint8_t* st = smem + CS * STAGE;
     const int q0 = cur_qi * BQ;
-    if (decltype(may_mask)::value && CAUSAL && q0 + shift < kw0 + 15)   // some pair of this wave is masked
+    // some (row, key) pair of this wave is masked (causal limit or window start)
+    if (decltype(may_mask)::value &&
+        ((CAUSAL && q0 + shift < kw0 + 15) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0)))
       body(st, q0, std::true_type{});
     else
       body(st, q0, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();          // the next tile has landed; this stage is free
-    if (++cur_h == G) {
-      cur_h = 0;
-      --cur_qi;
+    if constexpr (DOWN) {
+      if (++cur_h == G) {
+        cur_h = 0;
+        --cur_qi;
+      }
+    } else if (++cur_qi == n_qt) {
+      cur_qi = qt_begin;
+      ++cur_h;
     }
   };
   int it = 0;
-  if constexpr (CAUSAL) {
+  if constexpr (CAUSAL && !WIN) {
     // tiles whose first row sees every key of the workgroup need no mask; the
     // walk visits them first (whole groups of NSTAGE iterations)
     const int qi_full = (k0 + C::BK - 1 - shift + BQ - 1) / BQ;
@@ -974,21 +997,22 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using KD = typename std::conditional<D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
              typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>, DkdvCfg<D>>::type>::type;
   // 16 keys per wave at d = 128, and for causal d = 64 (measured on MI355X:
-  // causal GQA 32k backward -6%, causal B64 H16 T1024 d64 -20%; the
-  // non-causal d = 64 layer timed the same with either layout and keeps the
-  // 32-key one)
-  if constexpr (!WIN && !DROP && !ALT && (D == 128 || CAUSAL)) {
+  // causal GQA 32k backward -6%, its sliding-window form -22%, causal B64 H16
+  // T1024 d64 -20%; the non-causal d = 64 layer timed the same with either
+  // layout and keeps the 32-key one)
+  if constexpr (!DROP && !ALT && (D == 128 || CAUSAL)) {
     using K16 = Dkdv16Cfg<D>;
     const int n_ktiles = (a.Tk + K16::BK - 1) / K16::BK;
-    hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, K16>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(K16::NT), 0,
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, K16, WIN>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(K16::NT), 0,
                        stream, a, n_ktiles);
     return hipGetLastError();
+  } else {
+    using KC = typename std::conditional<ALT, DkdvCfg<D, KD::NW, (KD::BQ == 64 ? 32 : 64)>, KD>::type;
+    const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT),
+                       0, stream, a, n_ktiles);
+    return hipGetLastError();
   }
-  using KC = typename std::conditional<ALT, DkdvCfg<D, KD::NW, (KD::BQ == 64 ? 32 : 64)>, KD>::type;
-  const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT), 0,
-                     stream, a, n_ktiles);
-  return hipGetLastError();
 }
 
 }  // namespace fa
