@@ -938,11 +938,21 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     wait_vm_barrier<AHEAD_VM>();
   };
   int j = j_begin;
-  if constexpr (CAUSAL && !WIN) {
-    // key tiles every row of the workgroup sees whole need no mask; they come
-    // first (whole groups of NSTAGE tiles), in a loop of their own, so the
-    // masked body's registers do not weigh on it
-    const int j_full = j_begin + (min(n_kv, max(0, q0 + shift + 1) / BC) - j_begin) / C::NSTAGE * C::NSTAGE;
+  if constexpr (CAUSAL) {
+    // Key tiles every row of the workgroup sees whole need no mask; they run
+    // in a loop of their own (whole groups of NSTAGE tiles), so the masked
+    // body's registers do not weigh on it. With a window the tiles before the
+    // last row's window start come first, masked, in whole groups.
+    if constexpr (WIN) {
+      const int first_full = min(n_kv, (max(0, q0 + C::BR - 1 + shift - a.window + 1) + BC - 1) / BC);
+      const int j_head = j_begin + (first_full - j_begin + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE;
+      for (; j < j_head && j < n_kv; j += C::NSTAGE)
+        static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+          if (j + decltype(s)::value < n_kv) step(j + decltype(s)::value, s, std::true_type{});
+        });
+    }
+    const int j_end_full = min(n_kv, max(0, q0 + shift + 1) / BC);   // the tiles before it have no causal mask
+    const int j_full = j + max(0, j_end_full - j) / C::NSTAGE * C::NSTAGE;
     for (; j < j_full; j += C::NSTAGE)
       static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(j + decltype(s)::value, s, std::false_type{}); });
   }
@@ -972,17 +982,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 // check that the result does not depend on the tile shape: dQ takes 64-key
 // tiles where the default takes 32 and 32 where it takes 64, dK/dV walks
 // 32-row query tiles where the default walks 64 and 64 where it walks 32.
-// One workgroup per CU with 64-key tiles at d = 128, for the dQ passes whose
-// registers do not fit the two-workgroup tiling: the sliding window (it masks
-// tiles at both ends of a row's key range, so its loop is not split; the
-// two-workgroup tiling spills there and measured 1.8x slower) and dropout
-// (the Philox bytes of a tile).
+// One workgroup per CU with 64-key tiles at d = 128, for the dQ pass whose
+// registers do not fit the two-workgroup tiling: dropout (the Philox bytes of
+// a tile). The sliding window takes the two-workgroup tiling: its loop is
+// split like the causal one (masked head, unmasked middle, masked tail).
 template <int D>
 using DqOneCfg = DqCfg<D, DqCfg<D>::NW, (D == 64 ? 32 : 64), (D == 64 ? 2 : 3), DqCfg<D>::IGLP, 1>;
 
 template <int D, bool CAUSAL, bool WIN = false, bool DROP = false, bool ALT = false>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
-  using QD = typename std::conditional<WIN || DROP, DqOneCfg<D>, DqCfg<D>>::type;
+  using QD = typename std::conditional<DROP, DqOneCfg<D>, DqCfg<D>>::type;
   using QC = typename std::conditional<ALT, DqCfg<D, QD::NW, (QD::BC == 32 ? 64 : 32)>, QD>::type;
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + QC::BR - 1) / QC::BR;
