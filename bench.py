@@ -90,10 +90,10 @@ TRAFFIC_UNITS = {
     "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128, 3>", "decode_merge_kernel<128>"],
     "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false, false>@2097152"],
     "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false, false>",
-                                                   "bwd_dkdv16_kernel<128, true>"],
+                                                   "bwd_dkdv16_kernel<128, true, false>"],
     "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true, false>"],
     "fa_bwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["bwd_dq_kernel<128, true, true, false>",
-                                                     "bwd_dkdv_kernel<128, true, true, false>"],
+                                                     "bwd_dkdv16_kernel<128, true, true>"],
     "fa_fwd_fp8 causal B1 H32 T8192 d128": ["fwd_fp8_kernel<128, true>"],
     "fa_fwd_dropout B64 H16 T1024 d64 p0.1": ["fwd_bf16_kernel<64, false, false, true>"],
     "fa_bwd_dropout B64 H16 T1024 d64 p0.1": ["bwd_dq_kernel<64, false, false, true>",
