@@ -773,7 +773,7 @@ struct DqCfg {
 // direct-to-LDS loads into a ring of C::NSTAGE tiles, swizzled like the
 // dK/dV kernel's tiles. Keys past Tk read as zero rows and contribute nothing to dQ.
 template <int D, bool CAUSAL, class C = DqCfg<D>, bool WIN = false, bool DROP = false>
-__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+__global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int n_units) {
   static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
   constexpr int BC = C::BC, ROWB = C::ROWB, CH = C::CH, KTILE = C::KTILE, STAGE = C::STAGE;
@@ -785,25 +785,41 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
-  // Tile order: (batch, kv head) outermost, then query tile, then the query
-  // heads that share the kv head, so the workgroups that run together on an
-  // XCD read the same K/V tiles at about the same time.
+  // Work order: (batch, kv head) outermost, then the unit (query tile or
+  // pair of them), then the query heads that share the kv head, so the
+  // workgroups that run together on an XCD read the same K/V tiles at about
+  // the same time.
+  //   * Causal without window or dropout, a unit is a pair of query tiles:
+  //     tile p walks its key tiles up from the first, then tile n - 1 - p
+  //     walks its key tiles down from the last. Every workgroup then does the
+  //     same number of steps, and after s steps each reads key tile s (first
+  //     walk) or (n + 1) BR / BC - 1 - s (second walk) whatever its p (for
+  //     Tq = Tk): the resident workgroups share two K/V tiles at a time.
+  //   * Otherwise a unit is one query tile, causal ones longest first.
+  constexpr bool PAIR = CAUSAL && !WIN && !DROP;
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t G = (uint32_t)(a.Hq / a.Hkv), per_grp = (uint32_t)n_qtiles * G;
+  const uint32_t G = (uint32_t)(a.Hq / a.Hkv), per_grp = (uint32_t)n_units * G;
   const uint32_t kvg = t / per_grp, r = t - kvg * per_grp;
-  const int qt_lin = (int)(r / G), g = (int)(r - (uint32_t)qt_lin * G);
-  const int qt = CAUSAL ? (n_qtiles - 1 - qt_lin) : qt_lin;
+  const int unit = (int)(r / G), g = (int)(r - (uint32_t)unit * G);
   const int b = (int)kvg / a.Hkv, hk = (int)kvg - b * a.Hkv;
   const int h = hk * (int)G + g, bh = b * a.Hq + h;
-  const int q0 = qt * C::BR;
-  const int qw0 = q0 + wave * 32;                 // first row of this wave
-  const int qrow = qw0 + col;                     // this lane's query row
   const size_t qoff = (size_t)bh * a.Tq;
   const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
   const int shift = a.Tk - a.Tq;
+
+  // One query tile, its key tiles walked up (UP) or down.
+  auto query_tile = [&](const int qt, auto up_c) FA_INLINE {
+  constexpr bool UP = decltype(up_c)::value;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;                 // first row of this wave
+  const int qrow = qw0 + col;                     // this lane's query row
   int kv_end = a.Tk;
   if (CAUSAL) kv_end = min(a.Tk, q0 + C::BR + shift);
   const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  // tiles before j_begin are invisible to every row of the workgroup
+  const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
+  const int n_it = n_kv - j_begin;
+  auto tile_of = [&](int it) FA_INLINE { return UP ? j_begin + it : n_kv - 1 - it; };
 
   // Q and dO rows of this lane's query (B operands; the lane holds half of
   // the dims, lane ^ 32 the other half), its lse2 = LSE * log2(e) and
@@ -863,10 +879,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     dma_dst[i] = (dma_is_v[i] ? KTILE : 0) + m * 1024;
   }
   // Keys past Tk lie past the end of the buffer ranges and read as zeros, so
-  // only a tile past the loop needs an out-of-range base.
-  auto issue = [&](int j, auto stage_c) FA_INLINE {
+  // only an iteration past the walk needs an out-of-range base.
+  auto issue = [&](int it, auto stage_c) FA_INLINE {
     FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
-    const uint32_t tbase = j < n_kv ? (uint32_t)(j * BC) * D * 2 : kOutOfRange;
+    const uint32_t tbase = it < n_it ? (uint32_t)(tile_of(it) * BC) * D * 2 : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], tbase + dma_off[i]);
   };
@@ -881,8 +897,6 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
   const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
   const int lo = WIN ? qrow + shift - a.window + 1 : 0;   // window start of this lane's row
-  // tiles before j_begin are invisible to every row of the workgroup
-  const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
 
   // Dropout: the Philox bytes of this lane's row for the 32-key blocks of the
   // current tile (the forward's layout and contract); the next tile's are
@@ -968,13 +982,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
   }
-  if (j_begin < n_kv) {
-    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(j_begin + decltype(st)::value, st); });
+  if (n_it > 0) {
+    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(decltype(st)::value, st); });
     wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
   }
-  auto step = [&](int j, auto stage_c, auto may_mask) FA_INLINE {
+  auto step = [&](int it, auto stage_c, auto may_mask) FA_INLINE {
     constexpr int CS = decltype(stage_c)::value;
-    issue(j + C::NSTAGE - 1, std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});
+    issue(it + C::NSTAGE - 1, std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});
+    const int j = tile_of(it);
     const FA_LDS uint8_t* st = smem + CS * STAGE;
     // some (row, key) pair of this wave is masked (causal limit or window start)
     if (decltype(may_mask)::value &&
@@ -984,30 +999,37 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
       body(st, j, std::false_type{});
     wait_vm_barrier<AHEAD_VM>();
   };
-  int j = j_begin;
+  // Key tiles every row of the workgroup sees whole need no mask; they run in
+  // a loop of their own (whole groups of NSTAGE tiles), so the masked body's
+  // registers do not weigh on it. Walking up, the tiles before the last row's
+  // window start (window) come first, masked, and the causal diagonal last;
+  // walking down, the diagonal comes first.
+  int it = 0;
+  auto masked_groups = [&](int until) FA_INLINE {
+    for (; it < until; it += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+        if (it + decltype(s)::value < n_it) step(it + decltype(s)::value, s, std::true_type{});
+      });
+  };
+  auto unmasked_groups = [&](int until) FA_INLINE {
+    for (; it + C::NSTAGE <= until; it += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(it + decltype(s)::value, s, std::false_type{}); });
+  };
   if constexpr (CAUSAL) {
-    // Key tiles every row of the workgroup sees whole need no mask; they run
-    // in a loop of their own (whole groups of NSTAGE tiles), so the masked
-    // body's registers do not weigh on it. With a window the tiles before the
-    // last row's window start come first, masked, in whole groups.
-    if constexpr (WIN) {
-      const int first_full = min(n_kv, (max(0, q0 + C::BR - 1 + shift - a.window + 1) + BC - 1) / BC);
-      const int j_head = j_begin + (first_full - j_begin + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE;
-      for (; j < j_head && j < n_kv; j += C::NSTAGE)
-        static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
-          if (j + decltype(s)::value < n_kv) step(j + decltype(s)::value, s, std::true_type{});
-        });
-    }
     const int j_end_full = min(n_kv, max(0, q0 + shift + 1) / BC);   // the tiles before it have no causal mask
-    const int j_full = j + max(0, j_end_full - j) / C::NSTAGE * C::NSTAGE;
-    for (; j < j_full; j += C::NSTAGE)
-      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(j + decltype(s)::value, s, std::false_type{}); });
+    if constexpr (UP) {
+      if constexpr (WIN) {
+        const int first_full = min(n_kv, (max(0, q0 + C::BR - 1 + shift - a.window + 1) + BC - 1) / BC);
+        masked_groups((first_full - j_begin + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE);
+      }
+      unmasked_groups(j_end_full - j_begin);
+    } else {
+      masked_groups((n_kv - max(j_end_full, j_begin) + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE);
+      unmasked_groups(n_it);
+    }
   }
-  for (; j < n_kv; j += C::NSTAGE)
-    static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
-      if (j + decltype(s)::value < n_kv) step(j + decltype(s)::value, s, std::true_type{});
-    });
-  if (j_begin < n_kv) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
+  masked_groups(n_it);
+  if (n_it > 0) wait_vm_barrier<0>();   // no load is left writing LDS (the ring is free again)
 
   if (qrow < a.Tq) {
     uint16_t* dst = a.dq + (qoff + qrow) * D;
@@ -1020,6 +1042,15 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
         *(u32x2*)(dst + d0) = u32x2{pack_bf16x2(q[4 * g4] * a.scale, q[4 * g4 + 1] * a.scale),
                                     pack_bf16x2(q[4 * g4 + 2] * a.scale, q[4 * g4 + 3] * a.scale)};
       }
+  }
+  };
+
+  if constexpr (PAIR) {
+    query_tile(unit, std::true_type{});
+    const int qt2 = n_qtiles - 1 - unit;
+    if (qt2 != unit) query_tile(qt2, std::false_type{});
+  } else {
+    query_tile(CAUSAL ? n_qtiles - 1 - unit : unit, std::true_type{});
   }
 }
 
@@ -1042,8 +1073,10 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using QC = typename std::conditional<ALT, DqCfg<D, QD::NW, (QD::BC == 32 ? 64 : 32)>, QD>::type;
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + QC::BR - 1) / QC::BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QC, WIN, DROP>), dim3((unsigned)(n_qtiles * a.B * a.Hq)), dim3(QC::NT), 0,
-                     stream, a, n_qtiles);
+  // causal without window or dropout: one workgroup per pair of query tiles p, n - 1 - p
+  const int n_qunits = CAUSAL && !WIN && !DROP ? (n_qtiles + 1) / 2 : n_qtiles;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QC, WIN, DROP>), dim3((unsigned)(n_qunits * a.B * a.Hq)), dim3(QC::NT), 0,
+                     stream, a, n_qtiles, n_qunits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // masked d = 64 tiles: 32-row query tiles (the 64-row masked body spills at
