@@ -154,6 +154,26 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) {
   }
 }
 
+// Chunk swizzle for the 16x16x32 layouts (the 16-key dK/dV kernel's Q and dO
+// tiles, the 16-query forward's K and V tiles): chunk c of row r lives at
+// chunk c ^ swz16<D>(r). Measured on gfx950 with the LDS bank-conflict
+// counter, ds_read_b128 serves a wave in four passes of 16 lanes, told apart
+// by lane bit 5 and by the parity of lane bits 2, 3 and 4, and
+// ds_read_b64_tr_b16 in two passes (lanes 0-31, 32-63). These tables give
+// every lane of a pass its own banks in both read patterns of those kernels:
+// the A-operand reads (16 rows at chunks 4 ks + q) and the transposed reads
+// (8 consecutive rows at two neighbouring chunks). At d = 128 a row is one bank
+// row; at d = 64 two rows share one, so the table ignores row bit 0. The
+// 32x32 kernels' swizzles leave 2-way conflicts on both patterns here.
+template <int D>
+__device__ __forceinline__ uint32_t swz16(uint32_t r) {
+  if constexpr (D == 128) {
+    return (((r & 7u) << 1) | ((r >> 3) & 1u)) ^ (r & 8u);
+  } else {
+    return (((r >> 1) & 3u) << 1) ^ (((r >> 3) & 1u) * 5u);
+  }
+}
+
 // Philox-4x32-10 counter-based generator (Salmon, Moraes, Dror and Shaw,
 // "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11, section 3.2 and
 // Table 2): ten rounds, each multiplying words 0 and 2 of the counter by the
