@@ -41,6 +41,12 @@ BWD_SHAPES = [
     (1, 6, 2, 190, 190, 64, True),      # 3 query heads per KV head, ragged 64-row tiles
     (1, 6, 2, 300, 300, 128, False),
     (1, 2, 2, 600, 600, 64, False),     # several 256-key workgroups and a ragged one
+    # causal walks that pair tile p with tile n - 1 - p (dK/dV over 128-key
+    # tiles, dQ over query tiles): many pairs, an odd middle tile, Tq != Tk
+    (1, 4, 2, 1152, 1152, 128, True),   # 9 key tiles, 9 query tiles: four pairs and a middle one
+    (1, 2, 1, 700, 1000, 128, True),    # Tq < Tk across several pairs
+    (1, 4, 2, 900, 900, 64, True),      # the 16-key kernel at d = 64, ragged last tile
+    (1, 2, 2, 1000, 700, 64, True),     # Tq > Tk: the first 300 rows see no key
 ]
 
 
