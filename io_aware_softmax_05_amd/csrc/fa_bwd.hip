@@ -2,10 +2,11 @@
 //
 // The kernels and their launch template are in fa_bwd_kernels.hpp. This file
 // is compiled with the MFMAs in VGPR form (-mllvm -amdgpu-mfma-vgpr-form=1):
-// at d = 128 the kernels run four waves of up to 512 registers, and the
-// compiler's default puts MFMA results in AGPRs, whence every S and dP value
-// is copied back for the vector math. The VGPR form cuts those copies and
-// measured faster on the causal GQA backward; the sliding-window
+// where a wave needs more than 256 registers (the 32-key dK/dV kernel and the
+// one-workgroup dQ at d = 128, which dropout uses) the compiler's default puts
+// MFMA results in AGPRs, whence every S and dP value is copied back for the
+// vector math. The VGPR form cuts those copies and measured faster on the
+// causal GQA backward when it ran those kernels; the sliding-window
 // instantiations (fa_bwd_window.hip) measured faster with the default.
 #include "fa_bwd_kernels.hpp"
 

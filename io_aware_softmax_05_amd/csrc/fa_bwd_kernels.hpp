@@ -45,7 +45,8 @@ namespace fa {
 
 namespace {
 
-// 64-row query tiles in two LDS stages; d = 64: 8 waves of 32 keys with the
+// The 32-key layout (non-causal d = 64, dropout, the second tiling): 64-row
+// query tiles in two LDS stages; d = 64: 8 waves of 32 keys with the
 // small-GEMM interleave hint (iglp 0) ordering the LDS reads among the MFMAs;
 // d = 128: 4 waves (the dK/dV accumulators need up to 512 registers per
 // wave; 8 waves spill) and no hint. Both measured fastest on MI355X.
