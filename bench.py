@@ -409,6 +409,16 @@ def run_small_f32(raw, steps, warmup):
 
 # ------------------------------------------------------------ clock reading
 
+def frac_at_clock(achieved, peak, mhz):
+    """achieved / (peak scaled from the spec clock to the mean of the sampled clocks); None without samples."""
+    if not mhz:
+        return None
+    mean = sum(mhz) / len(mhz)
+    if mean <= 0:
+        return None
+    return round(achieved / (peak * mean / SPEC_SCLK_MHZ), 4)
+
+
 def read_sclk_under_load(launch, seconds=2.0):
     """Engine clock reported by amd-smi while `launch` (the headline kernel) is
     issued back to back: the matrix peak assumes the 2400 MHz top clock, and
@@ -986,8 +996,12 @@ def main():
     }
     res["roofline"]["median_ms"] = round(t["fwd"].median_ms(), 4)
     if extras and not args.no_clock:
-        res["roofline"]["sclk_under_load"] = read_sclk_under_load(calls[0][1])
+        sclk = read_sclk_under_load(calls[0][1])
+        res["roofline"]["sclk_under_load"] = sclk
         res["roofline"]["sclk_spec_mhz"] = SPEC_SCLK_MHZ
+        at = frac_at_clock(res["roofline"]["achieved"], res["roofline"]["peak"], sclk.get("mhz"))
+        if at is not None:   # the same peak scaled to the clock amd-smi read under the load
+            res["roofline"]["frac_at_sclk_under_load"] = at
     del dev
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -63,3 +63,11 @@ def test_recorded_traffic_is_null_for_stale_or_unknown_units(tmp_path, monkeypat
                                                     (2, 3, 8192, 128, True, 4 * 128 * 8192 * 8193 // 2 * 6)])
 def test_flop_convention(B, Hq, T, d, causal, want):
     assert bench.fwd_flops(B, Hq, T, T, d, causal) == want
+
+
+def test_fraction_at_the_measured_clock():
+    # the matrix peak scales with the engine clock: at 2000 MHz of 2400 it is 5/6 of the spec figure
+    assert bench.frac_at_clock(1000.0, 2500.0, [2000.0, 2000.0]) == round(1000.0 / (2500.0 * 2000 / 2400), 4)
+    assert bench.frac_at_clock(1000.0, 2500.0, [2400.0]) == 0.4
+    assert bench.frac_at_clock(1000.0, 2500.0, None) is None
+    assert bench.frac_at_clock(1000.0, 2500.0, []) is None
