@@ -119,13 +119,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
     }
   };
 
-  // Loads: physical chunk p of a tile holds logical chunk p ^ swz(row) of its row.
+  // Loads: physical chunk p of a tile holds logical chunk p ^ swz16(row) of its row
+  // (the chunk swizzle of the 16x16x32 operand reads, conflict free for both below).
   uint32_t dma_off[C::DMA];
 #pragma unroll
   for (int i = 0; i < C::DMA; ++i) {
     const int p = 64 * i + lane;
     const int r = p / CH, pc = p % CH;
-    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+    dma_off[i] = (uint32_t)(r * D + (pc ^ swz16<D>(r)) * 8) * 2;
   }
   DecCursor ld{(int)blockIdx.x, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   locate(ld);
@@ -164,10 +165,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
   // LDS read offsets. K rows (A operand of S^T = K q^T): row 16 blk + qcol,
   // chunk 4 ks + quad. V^T (A operand of O^T = V^T P^T): transposed reads of
   // rows tr_row (+16), chunk 2 db + ((qcol >> 1) & 1).
-  const uint32_t fk = swz<D>(qcol);
+  const uint32_t fk = swz16<D>(qcol);
   const uint32_t k_rd = qcol * ROWB + 64 * (fk >> 2) + 16 * (quad ^ (fk & 3));            // ^ 64 ks
   const int tr_row = 4 * quad + (qcol >> 2);
-  const uint32_t fv = swz<D>(tr_row);
+  const uint32_t fv = swz16<D>(tr_row);
   const uint32_t v_rd = tr_row * ROWB + 32 * (fv >> 1) + 16 * (((qcol >> 1) & 1) ^ (fv & 1)) + 8 * (qcol & 1);  // ^ 32 db
 
   bf16x8 qf[D / 32];
