@@ -147,8 +147,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
       dma_b128_stream(vrs, st + TILE + i * 1024, dma_off[i]);
     }
     if (live && ld.t == 0) {
-      // first tile of an item: its query rows come along (unswizzled); a wait
-      // that counts only tile loads stays safe, it just waits a little longer
+      // first tile of an item: its query rows come along (swizzled like the
+      // tiles); a wait that counts only tile loads stays safe, it just waits
+      // a little longer
       const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + ((size_t)ld.b * a.Hq + ld.hk * G) * D, (uint32_t)G * D * 2);
       // q_rows rows of CH chunks, 64 chunks (1 KiB) per wave load; lanes past
       // the last row read out of range and write zeros inside the slot
@@ -156,7 +157,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
         const int p = 64 * i + lane;
         const int r = ld.rg * 16 + p / CH;
         const bool ok = p < q_rows * CH && p / CH + ld.rg * 16 < G;
-        dma_b128(qrs, st + 2 * TILE + i * 1024, ok ? (uint32_t)(r * D + (p % CH) * 8) * 2 : kOutOfRange);
+        const uint32_t chunk = (uint32_t)(p % CH) ^ swz16<D>((uint32_t)(p / CH));
+        dma_b128(qrs, st + 2 * TILE + i * 1024, ok ? (uint32_t)(r * D + chunk * 8) * 2 : kOutOfRange);
       }
     }
     advance(ld);
@@ -166,6 +168,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
   // chunk 4 ks + quad. V^T (A operand of O^T = V^T P^T): transposed reads of
   // rows tr_row (+16), chunk 2 db + ((qcol >> 1) & 1).
   const uint32_t fk = swz16<D>(qcol);
+  const uint32_t q_rd = qcol * ROWB + 16 * (quad ^ fk);   // query row qcol, chunk 4 ks + quad (^ 64 ks)
   const uint32_t k_rd = qcol * ROWB + 64 * (fk >> 2) + 16 * (quad ^ (fk & 3));            // ^ 64 ks
   const int tr_row = 4 * quad + (qcol >> 2);
   const uint32_t fv = swz16<D>(tr_row);
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
       const FA_LDS uint8_t* qs = smem + cs * STAGE + 2 * TILE;
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        qf[ks] = as_bf16x8(live_row ? lds_read_b128(qs, qcol * ROWB + (32 * ks + 8 * quad) * 2) : u32x4{0, 0, 0, 0});
+        qf[ks] = as_bf16x8(live_row ? lds_read_b128(qs, q_rd ^ (64 * ks)) : u32x4{0, 0, 0, 0});
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
       m = -INFINITY;
