@@ -791,240 +791,240 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
 
   // One query tile, its key tiles walked up (UP) or down.
   auto query_tile = [&](const int qt, auto up_c) FA_INLINE {
-  constexpr bool UP = decltype(up_c)::value;
-  const int q0 = qt * C::BR;
-  const int qw0 = q0 + wave * 32;                 // first row of this wave
-  const int qrow = qw0 + col;                     // this lane's query row
-  int kv_end = a.Tk;
-  if (CAUSAL) kv_end = min(a.Tk, q0 + C::BR + shift);
-  const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
-  // tiles before j_begin are invisible to every row of the workgroup
-  const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
-  const int n_it = n_kv - j_begin;
-  auto tile_of = [&](int it) FA_INLINE { return UP ? j_begin + it : n_kv - 1 - it; };
+    constexpr bool UP = decltype(up_c)::value;
+    const int q0 = qt * C::BR;
+    const int qw0 = q0 + wave * 32;                 // first row of this wave
+    const int qrow = qw0 + col;                     // this lane's query row
+    int kv_end = a.Tk;
+    if (CAUSAL) kv_end = min(a.Tk, q0 + C::BR + shift);
+    const int n_kv = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+    // tiles before j_begin are invisible to every row of the workgroup
+    const int j_begin = WIN ? min(n_kv, max(0, q0 + shift - a.window + 1) / BC) : 0;
+    const int n_it = n_kv - j_begin;
+    auto tile_of = [&](int it) FA_INLINE { return UP ? j_begin + it : n_kv - 1 - it; };
 
-  // Q and dO rows of this lane's query (B operands; the lane holds half of
-  // the dims, lane ^ 32 the other half), its lse2 = LSE * log2(e) and
-  // D = sum_c dO_c O_c, which are also stored for the dK/dV kernel. A row
-  // that saw no key (LSE = -inf) gets lse2 = +inf, so every rebuilt
-  // probability is 0.
-  bf16x8 qf[D / 16], gf[D / 16];
-  float lse2, delta;
-  {
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff * D, (uint32_t)a.Tq * D * 2);
-    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + qoff * D, (uint32_t)a.Tq * D * 2);
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.o + qoff * D, (uint32_t)a.Tq * D * 2);
-    const bool live = qrow < a.Tq;
-    const uint32_t base = live ? (uint32_t)(qrow * D + 8 * half) * 2 : kOutOfRange;
-    float dsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 qw = buf_load_b128(qrs, base + ks * 32);
-      const u32x4 gw = buf_load_b128(grs, base + ks * 32);
-      const u32x4 ow = buf_load_b128(ors, base + ks * 32);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dsum = fmaf(bf16_lo(gw[e]), bf16_lo(ow[e]), dsum);
-        dsum = fmaf(bf16_hi(gw[e]), bf16_hi(ow[e]), dsum);
-      }
-      qf[ks] = as_bf16x8(qw);
-      gf[ks] = as_bf16x8(gw);
-    }
-    delta = pair_sum32(dsum);
-    // rows past Tq: Q = dO = 0, so dS = 0 whatever lse2 holds
-    const float lse = live ? a.lse[qoff + qrow] : 0.f;
-    lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-    if (live && half == 0) {   // two planes: lse2 for every row, then -D
-      a.stats[qoff + qrow] = lse2;
-      a.stats[(size_t)a.B * a.Hq * a.Tq + qoff + qrow] = -delta;
-    }
-  }
-
-  f32x16 dq_acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
-
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
-  uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
-  bool dma_is_v[C::DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const int n = wave * C::DMA_PER_WAVE + i;
-    const int m = n % (C::TILE_DMA / 2);
-    dma_is_v[i] = n >= C::TILE_DMA / 2;
-    const int p = 64 * m + lane;
-    const int r = p / CH, pc = p % CH;
-    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
-    dma_dst[i] = (dma_is_v[i] ? KTILE : 0) + m * 1024;
-  }
-  // Keys past Tk lie past the end of the buffer ranges and read as zeros, so
-  // only an iteration past the walk needs an out-of-range base.
-  auto issue = [&](int it, auto stage_c) FA_INLINE {
-    FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
-    const uint32_t tbase = it < n_it ? (uint32_t)(tile_of(it) * BC) * D * 2 : kOutOfRange;
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], tbase + dma_off[i]);
-  };
-
-  const uint32_t fq = swz<D>(col);
-  const uint32_t k_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
-  const int grp = lane >> 4, gi = lane & 15;
-  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
-  const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
-  const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
-  const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
-  const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
-  const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
-  const int lo = WIN ? qrow + shift - a.window + 1 : 0;   // window start of this lane's row
-
-  // Dropout: the Philox bytes of this lane's row for the 32-key blocks of the
-  // current tile (the forward's layout and contract); the next tile's are
-  // drawn while the matrix cores run this tile's dQ product.
-  u32x4 zcur[KB];
-  auto drop_bytes = [&](int j, int kb) -> u32x4 {
-    // plain XORs here: the bitop3 form costs this kernel a register past the
-    // two-workgroups-per-CU budget at d = 64 (and spills in dK/dV)
-    return dropout_bytes_32keys<false>((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
-                                a.drop.seed_lo, a.drop.seed_hi, half);
-  };
-
-  // At d = 128 without dropout every dP^T chain starts from a register block
-  // holding -D (one query per lane, so one value), read as the first
-  // product's accumulator input: dP - D comes out of the matrix cores at no
-  // per-tile cost. (d = 64 has no 16 registers to spare at two workgroups per
-  // CU; dropout needs dP itself.)
-  constexpr bool FOLD = D == 128 && !DROP;
-  f32x16 ndelta;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ndelta[r] = FOLD ? -delta : 0.f;
-
-  auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) FA_INLINE {
-    const FA_LDS uint8_t* kt = st;
-    const FA_LDS uint8_t* vt = st + KTILE;
-    f32x16 s[KB], dp[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    // Q and dO rows of this lane's query (B operands; the lane holds half of
+    // the dims, lane ^ 32 the other half), its lse2 = LSE * log2(e) and
+    // D = sum_c dO_c O_c, which are also stored for the dK/dV kernel. A row
+    // that saw no key (LSE = -inf) gets lse2 = +inf, so every rebuilt
+    // probability is 0.
+    bf16x8 qf[D / 16], gf[D / 16];
+    float lse2, delta;
+    {
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff * D, (uint32_t)a.Tq * D * 2);
+      const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + qoff * D, (uint32_t)a.Tq * D * 2);
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.o + qoff * D, (uint32_t)a.Tq * D * 2);
+      const bool live = qrow < a.Tq;
+      const uint32_t base = live ? (uint32_t)(qrow * D + 8 * half) * 2 : kOutOfRange;
+      float dsum = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
-        s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], ks == 0 ? f32x16{} : s[kb]);
-        dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? (FOLD ? ndelta : f32x16{}) : dp[kb]);
+        const u32x4 qw = buf_load_b128(qrs, base + ks * 32);
+        const u32x4 gw = buf_load_b128(grs, base + ks * 32);
+        const u32x4 ow = buf_load_b128(ors, base + ks * 32);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dsum = fmaf(bf16_lo(gw[e]), bf16_lo(ow[e]), dsum);
+          dsum = fmaf(bf16_hi(gw[e]), bf16_hi(ow[e]), dsum);
+        }
+        qf[ks] = as_bf16x8(qw);
+        gf[ks] = as_bf16x8(gw);
+      }
+      delta = pair_sum32(dsum);
+      // rows past Tq: Q = dO = 0, so dS = 0 whatever lse2 holds
+      const float lse = live ? a.lse[qoff + qrow] : 0.f;
+      lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      if (live && half == 0) {   // two planes: lse2 for every row, then -D
+        a.stats[qoff + qrow] = lse2;
+        a.stats[(size_t)a.B * a.Hq * a.Tq + qoff + qrow] = -delta;
       }
     }
-    uint32_t dsw[KB][8];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 zb = zcur[kb];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = exp2_fast(fmaf(s[kb][r], a.c, -lse2));
-        float p1 = exp2_fast(fmaf(s[kb][r + 1], a.c, -lse2));
-        if constexpr (decltype(masked)::value) {
-          const int kr = j * BC + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (kr > lim || (WIN && kr < lo)) p0 = 0.f;
-          if (kr + 1 > lim || (WIN && kr + 1 < lo)) p1 = 0.f;
-        }
-        float dp0 = dp[kb][r], dp1 = dp[kb][r + 1];
-        if constexpr (DROP) {   // dP of a dropped entry is 0, of a kept one scaled by 256 / t
-          dp0 = dropout_keep(zb, r, a.drop.t) ? dp0 * a.drop.inv_keep : 0.f;
-          dp1 = dropout_keep(zb, r + 1, a.drop.t) ? dp1 * a.drop.inv_keep : 0.f;
-        }
-        const float dsub = FOLD ? 0.f : delta;   // folded: dp already holds dP - D
-        dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp0 - dsub), p1 * (dp1 - dsub));
-      }
-    }
-    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
-    // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 sb = as_bf16x8(u32x4{dsw[kb][4 * hs], dsw[kb][4 * hs + 1], dsw[kb][4 * hs + 2], dsw[kb][4 * hs + 3]});
-        const uint32_t rb = (kb * 32 + hs * 16) * ROWB;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const u32x2 lo = lds_read_tr(kt, rb + (tr_lo ^ (64 * db)));
-          const u32x2 hi = lds_read_tr(kt, rb + (tr_hi ^ (64 * db)));
-          dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
-        }
-      }
-    if constexpr (DROP) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j + 1, kb);
-    }
-  };
 
-  // Ring of NSTAGE tiles, NSTAGE - 1 loads ahead of the compute. The loop is
-  // unrolled NSTAGE times, so every stage is a compile-time LDS offset.
-  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
-  if constexpr (DROP) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
-  }
-  if (n_it > 0) {
-    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(decltype(st)::value, st); });
-    wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
-  }
-  auto step = [&](int it, auto stage_c, auto may_mask) FA_INLINE {
-    constexpr int CS = decltype(stage_c)::value;
-    issue(it + C::NSTAGE - 1, std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});
-    const int j = tile_of(it);
-    const FA_LDS uint8_t* st = smem + CS * STAGE;
-    // some (row, key) pair of this wave is masked (causal limit or window start)
-    if (decltype(may_mask)::value &&
-        ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1)))
-      body(st, j, std::true_type{});
-    else
-      body(st, j, std::false_type{});
-    wait_vm_barrier<AHEAD_VM>();
-  };
-  // Key tiles every row of the workgroup sees whole need no mask; they run in
-  // a loop of their own (whole groups of NSTAGE tiles), so the masked body's
-  // registers do not weigh on it. Walking up, the tiles before the last row's
-  // window start (window) come first, masked, and the causal diagonal last;
-  // walking down, the diagonal comes first.
-  int it = 0;
-  auto masked_groups = [&](int until) FA_INLINE {
-    for (; it < until; it += C::NSTAGE)
-      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
-        if (it + decltype(s)::value < n_it) step(it + decltype(s)::value, s, std::true_type{});
-      });
-  };
-  auto unmasked_groups = [&](int until) FA_INLINE {
-    for (; it + C::NSTAGE <= until; it += C::NSTAGE)
-      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(it + decltype(s)::value, s, std::false_type{}); });
-  };
-  if constexpr (CAUSAL) {
-    const int j_end_full = min(n_kv, max(0, q0 + shift + 1) / BC);   // the tiles before it have no causal mask
-    if constexpr (UP) {
-      if constexpr (WIN) {
-        const int first_full = min(n_kv, (max(0, q0 + C::BR - 1 + shift - a.window + 1) + BC - 1) / BC);
-        masked_groups((first_full - j_begin + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE);
-      }
-      unmasked_groups(j_end_full - j_begin);
-    } else {
-      masked_groups((n_kv - max(j_end_full, j_begin) + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE);
-      unmasked_groups(n_it);
-    }
-  }
-  masked_groups(n_it);
-  if (n_it > 0) wait_vm_barrier<0>();   // no load is left writing LDS (the ring is free again)
-
-  if (qrow < a.Tq) {
-    uint16_t* dst = a.dq + (qoff + qrow) * D;
+    f32x16 dq_acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        const f32x16& q = dq_acc[db];
-        *(u32x2*)(dst + d0) = u32x2{pack_bf16x2(q[4 * g4] * a.scale, q[4 * g4 + 1] * a.scale),
-                                    pack_bf16x2(q[4 * g4 + 2] * a.scale, q[4 * g4 + 3] * a.scale)};
+      for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
+
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+    uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+    bool dma_is_v[C::DMA_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int n = wave * C::DMA_PER_WAVE + i;
+      const int m = n % (C::TILE_DMA / 2);
+      dma_is_v[i] = n >= C::TILE_DMA / 2;
+      const int p = 64 * m + lane;
+      const int r = p / CH, pc = p % CH;
+      dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+      dma_dst[i] = (dma_is_v[i] ? KTILE : 0) + m * 1024;
+    }
+    // Keys past Tk lie past the end of the buffer ranges and read as zeros, so
+    // only an iteration past the walk needs an out-of-range base.
+    auto issue = [&](int it, auto stage_c) FA_INLINE {
+      FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
+      const uint32_t tbase = it < n_it ? (uint32_t)(tile_of(it) * BC) * D * 2 : kOutOfRange;
+#pragma unroll
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_v[i] ? vrs : krs, st + dma_dst[i], tbase + dma_off[i]);
+    };
+
+    const uint32_t fq = swz<D>(col);
+    const uint32_t k_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
+    const int grp = lane >> 4, gi = lane & 15;
+    const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+    const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
+    const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
+    const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
+    const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
+    const int lim = CAUSAL ? min(a.Tk - 1, qrow + shift) : a.Tk - 1;
+    const int lo = WIN ? qrow + shift - a.window + 1 : 0;   // window start of this lane's row
+
+    // Dropout: the Philox bytes of this lane's row for the 32-key blocks of the
+    // current tile (the forward's layout and contract); the next tile's are
+    // drawn while the matrix cores run this tile's dQ product.
+    u32x4 zcur[KB];
+    auto drop_bytes = [&](int j, int kb) -> u32x4 {
+      // plain XORs here: the bitop3 form costs this kernel a register past the
+      // two-workgroups-per-CU budget at d = 64 (and spills in dK/dV)
+      return dropout_bytes_32keys<false>((uint32_t)(j * BC + kb * 32), (uint32_t)qrow, (uint32_t)bh, a.drop.offset,
+                                  a.drop.seed_lo, a.drop.seed_hi, half);
+    };
+
+    // At d = 128 without dropout every dP^T chain starts from a register block
+    // holding -D (one query per lane, so one value), read as the first
+    // product's accumulator input: dP - D comes out of the matrix cores at no
+    // per-tile cost. (d = 64 has no 16 registers to spare at two workgroups per
+    // CU; dropout needs dP itself.)
+    constexpr bool FOLD = D == 128 && !DROP;
+    f32x16 ndelta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndelta[r] = FOLD ? -delta : 0.f;
+
+    auto body = [&](const FA_LDS uint8_t* st, int j, auto masked) FA_INLINE {
+      const FA_LDS uint8_t* kt = st;
+      const FA_LDS uint8_t* vt = st + KTILE;
+      f32x16 s[KB], dp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
+          s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], ks == 0 ? f32x16{} : s[kb]);
+          dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? (FOLD ? ndelta : f32x16{}) : dp[kb]);
+        }
       }
-  }
+      uint32_t dsw[KB][8];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 zb = zcur[kb];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = exp2_fast(fmaf(s[kb][r], a.c, -lse2));
+          float p1 = exp2_fast(fmaf(s[kb][r + 1], a.c, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int kr = j * BC + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (kr > lim || (WIN && kr < lo)) p0 = 0.f;
+            if (kr + 1 > lim || (WIN && kr + 1 < lo)) p1 = 0.f;
+          }
+          float dp0 = dp[kb][r], dp1 = dp[kb][r + 1];
+          if constexpr (DROP) {   // dP of a dropped entry is 0, of a kept one scaled by 256 / t
+            dp0 = dropout_keep(zb, r, a.drop.t) ? dp0 * a.drop.inv_keep : 0.f;
+            dp1 = dropout_keep(zb, r + 1, a.drop.t) ? dp1 * a.drop.inv_keep : 0.f;
+          }
+          const float dsub = FOLD ? 0.f : delta;   // folded: dp already holds dP - D
+          dsw[kb][r >> 1] = pack_bf16x2(p0 * (dp0 - dsub), p1 * (dp1 - dsub));
+        }
+      }
+      if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
+      // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const bf16x8 sb = as_bf16x8(u32x4{dsw[kb][4 * hs], dsw[kb][4 * hs + 1], dsw[kb][4 * hs + 2], dsw[kb][4 * hs + 3]});
+          const uint32_t rb = (kb * 32 + hs * 16) * ROWB;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const u32x2 lo = lds_read_tr(kt, rb + (tr_lo ^ (64 * db)));
+            const u32x2 hi = lds_read_tr(kt, rb + (tr_hi ^ (64 * db)));
+            dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
+          }
+        }
+      if constexpr (DROP) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j + 1, kb);
+      }
+    };
+
+    // Ring of NSTAGE tiles, NSTAGE - 1 loads ahead of the compute. The loop is
+    // unrolled NSTAGE times, so every stage is a compile-time LDS offset.
+    constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
+    }
+    if (n_it > 0) {
+      static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(decltype(st)::value, st); });
+      wait_vm_barrier<AHEAD_VM>();          // Q/dO rows, statistics and the first tile have landed
+    }
+    auto step = [&](int it, auto stage_c, auto may_mask) FA_INLINE {
+      constexpr int CS = decltype(stage_c)::value;
+      issue(it + C::NSTAGE - 1, std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});
+      const int j = tile_of(it);
+      const FA_LDS uint8_t* st = smem + CS * STAGE;
+      // some (row, key) pair of this wave is masked (causal limit or window start)
+      if (decltype(may_mask)::value &&
+          ((CAUSAL && j * BC + BC - 1 > qw0 + shift) || (WIN && j * BC < qw0 + 31 + shift - a.window + 1)))
+        body(st, j, std::true_type{});
+      else
+        body(st, j, std::false_type{});
+      wait_vm_barrier<AHEAD_VM>();
+    };
+    // Key tiles every row of the workgroup sees whole need no mask; they run in
+    // a loop of their own (whole groups of NSTAGE tiles), so the masked body's
+    // registers do not weigh on it. Walking up, the tiles before the last row's
+    // window start (window) come first, masked, and the causal diagonal last;
+    // walking down, the diagonal comes first.
+    int it = 0;
+    auto masked_groups = [&](int until) FA_INLINE {
+      for (; it < until; it += C::NSTAGE)
+        static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+          if (it + decltype(s)::value < n_it) step(it + decltype(s)::value, s, std::true_type{});
+        });
+    };
+    auto unmasked_groups = [&](int until) FA_INLINE {
+      for (; it + C::NSTAGE <= until; it += C::NSTAGE)
+        static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(it + decltype(s)::value, s, std::false_type{}); });
+    };
+    if constexpr (CAUSAL) {
+      const int j_end_full = min(n_kv, max(0, q0 + shift + 1) / BC);   // the tiles before it have no causal mask
+      if constexpr (UP) {
+        if constexpr (WIN) {
+          const int first_full = min(n_kv, (max(0, q0 + C::BR - 1 + shift - a.window + 1) + BC - 1) / BC);
+          masked_groups((first_full - j_begin + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE);
+        }
+        unmasked_groups(j_end_full - j_begin);
+      } else {
+        masked_groups((n_kv - max(j_end_full, j_begin) + C::NSTAGE - 1) / C::NSTAGE * C::NSTAGE);
+        unmasked_groups(n_it);
+      }
+    }
+    masked_groups(n_it);
+    if (n_it > 0) wait_vm_barrier<0>();   // no load is left writing LDS (the ring is free again)
+
+    if (qrow < a.Tq) {
+      uint16_t* dst = a.dq + (qoff + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * half;
+          const f32x16& q = dq_acc[db];
+          *(u32x2*)(dst + d0) = u32x2{pack_bf16x2(q[4 * g4] * a.scale, q[4 * g4 + 1] * a.scale),
+                                      pack_bf16x2(q[4 * g4 + 2] * a.scale, q[4 * g4 + 3] * a.scale)};
+        }
+    }
   };
 
   if constexpr (PAIR) {
