@@ -93,8 +93,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   static_assert(CAUSAL || !WIN, "a sliding window is a causal band");
   static_assert(!(WIN && DROP), "dropout is not offered with a sliding window");
   constexpr int BQ = C::BQ, QB = C::QB, ROWB = C::ROWB, CH = C::CH, QTILE = C::QTILE, STAGE = C::STAGE;
-  // dropout: a wave-private 32 x 32 byte tile turns row-major Philox bytes into key columns
-  constexpr int ZTILE = 32 * 32;
+  // dropout: a wave-private 32 x 32 byte tile turns row-major Philox bytes into key columns;
+  // rows are 48 bytes apart, which keeps its 128-bit writes and byte reads free of bank conflicts
+  constexpr int ZPITCH = 48, ZTILE = 32 * ZPITCH;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::NSTAGE * STAGE + (DROP ? C::NW * ZTILE : 0)];
   FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
 
@@ -267,9 +268,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
       if constexpr (DROP) {
         const u32x4 w = philox4x32_10<false>((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
                                       a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
-        lds_write_b128(ztile, col * 32 + 16 * half, w);
+        lds_write_b128(ztile, col * ZPITCH + 16 * half, w);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) zbyte[i] = ztile[(8 * (i >> 2) + 4 * half + (i & 3)) * 32 + col];
+        for (int i = 0; i < 16; ++i) zbyte[i] = ztile[(8 * (i >> 2) + 4 * half + (i & 3)) * ZPITCH + col];
       }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
