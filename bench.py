@@ -57,6 +57,7 @@ import hashlib
 import json
 import os
 import platform
+import statistics
 import subprocess
 import sys
 import threading
@@ -410,7 +411,10 @@ def run_small_f32(raw, steps, warmup):
 # ------------------------------------------------------------ clock reading
 
 def frac_at_clock(achieved, peak, mhz):
-    """achieved / (peak scaled from the spec clock to the mean of the sampled clocks); None without samples."""
+    """achieved / (peak scaled from the spec clock to `mhz`: one clock, or the
+    mean of a list of them); None without a clock."""
+    if isinstance(mhz, (int, float)):
+        mhz = [mhz]
     if not mhz:
         return None
     mean = sum(mhz) / len(mhz)
@@ -419,32 +423,8 @@ def frac_at_clock(achieved, peak, mhz):
     return round(achieved / (peak * mean / SPEC_SCLK_MHZ), 4)
 
 
-def read_sclk_under_load(launch, seconds=2.0):
-    """Engine clock reported by amd-smi while `launch` (the headline kernel) is
-    issued back to back: the matrix peak assumes the 2400 MHz top clock, and
-    sustained matrix work runs below it. Returns {"mhz": [...], ...} or an error."""
-    import torch
-    box = {}
-
-    def reader():
-        time.sleep(0.5)   # let the clock settle under the load
-        try:
-            r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
-                               text=True, timeout=20)
-            box["out"], box["rc"] = r.stdout, r.returncode
-        except Exception as e:  # noqa: BLE001 - reported, never fatal
-            box["err"] = repr(e)
-
-    th = threading.Thread(target=reader)
-    t0 = time.perf_counter()
-    th.start()
-    while th.is_alive() and time.perf_counter() - t0 < 30:
-        for _ in range(50):
-            launch()
-        torch.cuda.synchronize()
-    th.join()
-    if "err" in box or box.get("rc", 1) != 0:
-        return {"mhz": None, "error": box.get("err") or f"amd-smi rc {box.get('rc')}"}
+def gfx_clocks(amd_smi_json):
+    """The gfx engine clocks (MHz, one per XCD) in the JSON of `amd-smi metric --clock`."""
     mhz = []
 
     def walk(x, key=""):
@@ -461,11 +441,55 @@ def read_sclk_under_load(launch, seconds=2.0):
         elif isinstance(x, list):
             for vv in x:
                 walk(vv, key)
-    try:
-        walk(json.loads(box["out"]))
-    except ValueError:
-        return {"mhz": None, "error": "amd-smi output is not JSON"}
-    return {"mhz": mhz or None, "source": "amd-smi metric --clock, sampled while the headline kernel runs"}
+    walk(amd_smi_json)
+    return mhz
+
+
+def read_sclk_under_load(launch, samples=6, gap=0.3):
+    """Engine clock reported by amd-smi while `launch` (the headline kernel) is
+    issued back to back: the matrix peak assumes the 2400 MHz top clock, and
+    sustained matrix work runs below it. amd-smi reads an instantaneous value,
+    so it is sampled `samples` times; "mhz" is the median of the samples' means
+    over the XCDs. Returns {"mhz": ..., "samples": [...], ...} or an error."""
+    import torch
+    box = {"out": []}
+
+    def reader():
+        time.sleep(0.5)   # let the clock settle under the load
+        try:
+            for _ in range(samples):
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=20)
+                if r.returncode != 0:
+                    box["rc"] = r.returncode
+                    return
+                box["out"].append(r.stdout)
+                time.sleep(gap)
+        except Exception as e:  # noqa: BLE001 - reported, never fatal
+            box["err"] = repr(e)
+
+    th = threading.Thread(target=reader)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < 60:
+        for _ in range(50):
+            launch()
+        torch.cuda.synchronize()
+    th.join()
+    if "err" in box or "rc" in box or not box["out"]:
+        return {"mhz": None, "error": box.get("err") or f"amd-smi rc {box.get('rc')}"}
+    per_sample = []
+    for out in box["out"]:
+        try:
+            clk = gfx_clocks(json.loads(out))
+        except ValueError:
+            return {"mhz": None, "error": "amd-smi output is not JSON"}
+        if clk:
+            per_sample.append(round(sum(clk) / len(clk), 1))
+    if not per_sample:
+        return {"mhz": None, "error": "no gfx clock in the amd-smi output"}
+    return {"mhz": statistics.median(per_sample), "samples": per_sample,
+            "source": "amd-smi metric --clock, sampled while the headline kernel runs (mean over XCDs per sample)"}
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -1002,6 +1026,13 @@ def main():
         at = frac_at_clock(res["roofline"]["achieved"], res["roofline"]["peak"], sclk.get("mhz"))
         if at is not None:   # the same peak scaled to the clock amd-smi read under the load
             res["roofline"]["frac_at_sclk_under_load"] = at
+    # the same peak scaled to the clock the counter run measured for this kernel
+    # (GRBM_GUI_ACTIVE over the dispatch's duration)
+    for c in (res["roofline"].get("counters") or {}).values():
+        at = frac_at_clock(res["roofline"]["achieved"], res["roofline"]["peak"], c.get("clock_mhz"))
+        if at is not None:
+            res["roofline"]["frac_at_counter_clock"] = at
+            break
     del dev
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -71,3 +71,15 @@ def test_fraction_at_the_measured_clock():
     assert bench.frac_at_clock(1000.0, 2500.0, [2400.0]) == 0.4
     assert bench.frac_at_clock(1000.0, 2500.0, None) is None
     assert bench.frac_at_clock(1000.0, 2500.0, []) is None
+    assert bench.frac_at_clock(1000.0, 2500.0, 2000) == round(1000.0 / (2500.0 * 2000 / 2400), 4)
+
+
+def test_gfx_clocks_reads_only_the_engine_clocks():
+    # amd-smi metric --clock --json: one "clk" per clock domain; only the gfx ones are the engine's
+    out = {"gpu_data": [{"gpu": 0, "clock": {
+        "gfx_0": {"clk": {"value": 1400, "unit": "MHz"}, "min_clk": {"value": 500}},
+        "gfx_1": {"clk": {"value": 2200, "unit": "MHz"}},
+        "mem_0": {"clk": {"value": 1900, "unit": "MHz"}},
+        "vclk_0": {"clk": {"value": 29, "unit": "MHz"}}}}]}
+    assert bench.gfx_clocks(out) == [1400.0, 2200.0]
+    assert bench.gfx_clocks({"gfx_0": {"clk": "N/A"}}) == []
