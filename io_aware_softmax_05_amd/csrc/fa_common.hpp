@@ -137,6 +137,29 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Items 0 .. NI - 1, each an operand read followed by the MFMA that uses it,
+// run with the reads one chunk of CK items ahead: the reads of chunk c + 1 are
+// issued before the MFMAs of chunk c. Left to itself the compiler issues each
+// LDS operand read right before its MFMA, which then waits out the whole LDS
+// latency; the scheduling fences between chunks keep the reads where they are
+// written (vector and scalar ALU work may still move across them). read(i)
+// and mma(i) get i as a std::integral_constant and keep the operands of chunk
+// c in buffer c & 1.
+constexpr int kFenceLetAluCross = 0x2 | 0x4;   // sched_barrier mask: VALU, SALU
+template <int NI, int CK, class Read, class Mma>
+__device__ __forceinline__ void chunk_pipeline(Read&& read, Mma&& mma) {
+  static_assert(NI % CK == 0, "whole chunks");
+  static_for<0, CK>([&](auto j) { read(j); });
+  static_for<0, NI / CK>([&](auto c_c) {
+    constexpr int c = decltype(c_c)::value;
+    if constexpr (c + 1 < NI / CK)
+      static_for<0, CK>([&](auto j) { read(std::integral_constant<int, CK * (c + 1) + decltype(j)::value>{}); });
+    __builtin_amdgcn_sched_barrier(kFenceLetAluCross);
+    static_for<0, CK>([&](auto j) { mma(std::integral_constant<int, CK * c + decltype(j)::value>{}); });
+    __builtin_amdgcn_sched_barrier(kFenceLetAluCross);
+  });
+}
+
 // XOR swizzle of the 16-byte chunks of a row of D bf16 values, for LDS tiles
 // stored without padding. Chunk c of row r lives at chunk c ^ swz<D>(r).
 // With 64 four-byte banks it makes both access patterns conflict free:
