@@ -936,14 +936,28 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
       const FA_LDS uint8_t* kt = st;
       const FA_LDS uint8_t* vt = st + KTILE;
       f32x16 s[KB], dp[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const uint32_t off = kb * 32 * ROWB + (k_rd ^ (32 * ks));
-          s[kb] = mfma32(as_bf16x8(lds_read_b128(kt, off)), qf[ks], ks == 0 ? f32x16{} : s[kb]);
-          dp[kb] = mfma32(as_bf16x8(lds_read_b128(vt, off)), gf[ks], ks == 0 ? (FOLD ? ndelta : f32x16{}) : dp[kb]);
-        }
+      // Both products take their LDS operands two items ahead of the MFMAs
+      // (chunk_pipeline; measured on MI355X: sliding-window backward -7.5%,
+      // causal 32k GQA -2%, dropout at d = 128 -9%), except the d = 64
+      // dropout pass, which ran 5% slower with it and keeps the compiler's
+      // order. S = K Q^T and dP - D: item i is (kb, ks, K or V) =
+      // (i / (2 KS), i / 2 % KS, i % 2), one 128-bit read and one MFMA.
+      constexpr bool AHEAD = !(DROP && D == 64);
+      constexpr int KS = D / 16, CK = 2;
+      {
+        u32x4 ab[2][CK];
+        auto rd = [&](auto i_c) FA_INLINE {
+          constexpr int i = decltype(i_c)::value, kb = i / (2 * KS), ks = i / 2 % KS, w = i % 2;
+          ab[i / CK & 1][i % CK] = lds_read_b128(w ? vt : kt, kb * 32 * ROWB + (k_rd ^ (32 * ks)));
+        };
+        auto mm = [&](auto i_c) FA_INLINE {
+          constexpr int i = decltype(i_c)::value, kb = i / (2 * KS), ks = i / 2 % KS, w = i % 2;
+          const bf16x8 x = as_bf16x8(ab[i / CK & 1][i % CK]);
+          if constexpr (w == 0) s[kb] = mfma32(x, qf[ks], ks == 0 ? f32x16{} : s[kb]);
+          else dp[kb] = mfma32(x, gf[ks], ks == 0 ? (FOLD ? ndelta : f32x16{}) : dp[kb]);
+        };
+        if constexpr (AHEAD) chunk_pipeline<2 * KB * KS, CK>(rd, mm);
+        else static_for<0, 2 * KB * KS>([&](auto i) FA_INLINE { rd(i); mm(i); });
       }
       uint32_t dsw[KB][8];
 #pragma unroll
@@ -968,20 +982,27 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
         }
       }
       if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
-      // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
+      // dQ^T[d, query] += K^T[d, key] dS^T[key, query], 16 keys per step: item
+      // i is (16-key step, db) = (i / NDB, i % NDB), two transposed reads and
+      // one MFMA.
+      {
+        constexpr int NDB = D / 32;
+        u32x4 tb[2][CK];
+        auto rd = [&](auto i_c) FA_INLINE {
+          constexpr int i = decltype(i_c)::value, kh = i / NDB, db = i % NDB;
+          const uint32_t rb = kh * 16 * ROWB;
+          const u32x2 lo = lds_read_tr(kt, rb + (tr_lo ^ (64 * db)));
+          const u32x2 hi = lds_read_tr(kt, rb + (tr_hi ^ (64 * db)));
+          tb[i / CK & 1][i % CK] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        auto mm = [&](auto i_c) FA_INLINE {
+          constexpr int i = decltype(i_c)::value, kh = i / NDB, db = i % NDB, kb = kh / 2, hs = kh % 2;
           const bf16x8 sb = as_bf16x8(u32x4{dsw[kb][4 * hs], dsw[kb][4 * hs + 1], dsw[kb][4 * hs + 2], dsw[kb][4 * hs + 3]});
-          const uint32_t rb = (kb * 32 + hs * 16) * ROWB;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const u32x2 lo = lds_read_tr(kt, rb + (tr_lo ^ (64 * db)));
-            const u32x2 hi = lds_read_tr(kt, rb + (tr_hi ^ (64 * db)));
-            dq_acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dq_acc[db]);
-          }
-        }
+          dq_acc[db] = mfma32(as_bf16x8(tb[i / CK & 1][i % CK]), sb, dq_acc[db]);
+        };
+        if constexpr (AHEAD) chunk_pipeline<2 * KB * NDB, CK>(rd, mm);
+        else static_for<0, 2 * KB * NDB>([&](auto i) FA_INLINE { rd(i); mm(i); });
+      }
       if constexpr (DROP) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j + 1, kb);
