@@ -14,6 +14,9 @@
 //     grid = query tiles x heads x batch, remapped so that the tiles of one
 //     kv head (all query heads that share it) run on one XCD and its L2,
 //     query heads of a group side by side, causal tiles longest first.
+//     Causal: waves w and w + NW / 2 (one SIMD) take row blocks b and
+//     NW - 1 - b, and past the diagonal a wave skips the tiles none of its
+//     rows sees, so the SIMDs share that stretch evenly.
 //   * 64-key K and V tiles stream HBM -> registers -> LDS through buffer
 //     loads (out-of-range rows read as zeros, so the loop has no branches),
 //     double buffered with one barrier per tile. Row pitches are chosen for
@@ -131,8 +134,22 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
     j_head = min(n_kv, max(j_begin, (max(0, lo_last) + BC - 1) / BC));
   }
 
+  // Causal: the two waves that share a SIMD (w and w + NW / 2) take row
+  // blocks b and NW - 1 - b, so every SIMD has the same share of the tiles
+  // past the diagonal, which a wave skips once none of its rows sees them.
+  constexpr bool SKIP = CAUSAL && !WIN && !DROP;
+  const int rblk = SKIP && wave >= C::NW / 2 ? C::NW - 1 - (wave - C::NW / 2) : wave;
+  const int qrow = q0 + rblk * 32 + col;
+  // Tiles [0, w_full) are complete and visible to every row of this wave,
+  // tiles [w_end, n_kv) to none of them.
+  int w_full = n_full, w_end = n_kv;
+  if (SKIP) {
+    const int r_first = q0 + rblk * 32 + shift;
+    w_full = __builtin_amdgcn_readfirstlane(max(n_full, min(a.Tk / BC, max(0, r_first + 1) / BC)));
+    w_end = __builtin_amdgcn_readfirstlane(min(n_kv, (min(a.Tk, max(0, r_first + 32)) + BC - 1) / BC));
+  }
+
   // Q fragments: B operand of S^T = K Q^T (lane: query column, 8 dims).
-  const int qrow = q0 + wave * 32 + col;
   bf16x8 qf[D / 16];
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff, (uint32_t)a.Tq * D * 2);
@@ -257,13 +274,20 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
   auto body = [&](int j, auto next_masked, auto has_next, f32x16* s_cur, f32x16* s_nxt, u32x4* z_cur,
                   u32x4* z_nxt) {
     constexpr bool HN = decltype(has_next)::value;
+    constexpr bool NM = decltype(next_masked)::value;
     load_k(j + 2);
     load_v(j + 1);
+    // masked stretch: this wave's rows may see none of tile j or j + 1
+    const bool cur_live = !(SKIP && NM) || j < w_end;
+    const bool nxt_live = !(SKIP && NM) || j + 1 < w_end;
     const float m_ref = (m == -INFINITY) ? 0.f : m;
     // stage A: S_{j+1} on the matrix cores, P_j = 2^(S_j c - m) on the vector unit
-    if constexpr (HN) scores((j + 1) & 1, s_nxt);
+    if constexpr (HN) {
+      if (nxt_live) scores((j + 1) & 1, s_nxt);
+    }
     bf16x8 pb[KB * 2];
     float lsum = 0.f;
+    if (cur_live) {
 #pragma unroll
     for (int kb_i = 0; kb_i < KB; ++kb_i) {
       // dropout: the row sum takes every probability, the product with V only the kept ones
@@ -301,6 +325,7 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
           oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kb_i * 2 + hs], oacc[db]);
         }
       }
+    }
     // the next tile's dropout bytes, drawn while the matrix cores run O += V_j P_j
     if constexpr (DROP && HN) {
 #pragma unroll
@@ -308,8 +333,13 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
     }
     kahan_add(l, lc, lsum);
     if constexpr (HN) {
-      if constexpr (decltype(next_masked)::value) mask(j + 1, s_nxt);
-      const float m_new = fmaxf(m, rowmax(s_nxt) * a.c);
+      float m_new = m;
+      if (nxt_live) {
+        if constexpr (NM) {
+          if (!SKIP || j + 1 >= w_full) mask(j + 1, s_nxt);
+        }
+        m_new = fmaxf(m, rowmax(s_nxt) * a.c);
+      }
       const bool move = __builtin_amdgcn_ballot_w64(m_new > m + kRescaleSlack) != 0;
       store_k(j & 1);
       store_v((j + 1) & 1);
