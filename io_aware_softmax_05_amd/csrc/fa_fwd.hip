@@ -289,42 +289,42 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
     float lsum = 0.f;
     if (cur_live) {
 #pragma unroll
-    for (int kb_i = 0; kb_i < KB; ++kb_i) {
-      // dropout: the row sum takes every probability, the product with V only the kept ones
-      const u32x4 zb = z_cur[kb_i];
+      for (int kb_i = 0; kb_i < KB; ++kb_i) {
+        // dropout: the row sum takes every probability, the product with V only the kept ones
+        const u32x4 zb = z_cur[kb_i];
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        uint32_t pw[4];
+        for (int hs = 0; hs < 2; ++hs) {
+          uint32_t pw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * hs + 2 * e;
-          float p0 = exp2_fast(fmaf(s_cur[kb_i][r], a.c, -m_ref));
-          float p1 = exp2_fast(fmaf(s_cur[kb_i][r + 1], a.c, -m_ref));
-          lsum += p0 + p1;
-          if constexpr (DROP) {
-            if (!dropout_keep(zb, r, a.drop.t)) p0 = 0.f;
-            if (!dropout_keep(zb, r + 1, a.drop.t)) p1 = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * hs + 2 * e;
+            float p0 = exp2_fast(fmaf(s_cur[kb_i][r], a.c, -m_ref));
+            float p1 = exp2_fast(fmaf(s_cur[kb_i][r + 1], a.c, -m_ref));
+            lsum += p0 + p1;
+            if constexpr (DROP) {
+              if (!dropout_keep(zb, r, a.drop.t)) p0 = 0.f;
+              if (!dropout_keep(zb, r + 1, a.drop.t)) p1 = 0.f;
+            }
+            pw[e] = pack_bf16x2(p0, p1);
           }
-          pw[e] = pack_bf16x2(p0, p1);
-        }
-        pb[kb_i * 2 + hs] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-      }
-    }
-    __builtin_amdgcn_iglp_opt(2);
-    // stage B: O^T[d, query] += V^T[d, key] P^T[key, query], 16 keys per step
-    const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
-#pragma unroll
-    for (int kb_i = 0; kb_i < KB; ++kb_i)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const int row = kb_i * 32 + hs * 16;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const u32x2 lo = lds_read_tr(vb, row * VPITCH + db * 64);
-          const u32x2 hi = lds_read_tr(vb, (row + 8) * VPITCH + db * 64);
-          oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kb_i * 2 + hs], oacc[db]);
+          pb[kb_i * 2 + hs] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
         }
       }
+      __builtin_amdgcn_iglp_opt(2);
+      // stage B: O^T[d, query] += V^T[d, key] P^T[key, query], 16 keys per step
+      const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
+#pragma unroll
+      for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const int row = kb_i * 32 + hs * 16;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const u32x2 lo = lds_read_tr(vb, row * VPITCH + db * 64);
+            const u32x2 hi = lds_read_tr(vb, (row + 8) * VPITCH + db * 64);
+            oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kb_i * 2 + hs], oacc[db]);
+          }
+        }
     }
     // the next tile's dropout bytes, drawn while the matrix cores run O += V_j P_j
     if constexpr (DROP && HN) {
