@@ -24,10 +24,9 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip",
            "fa_bwd_window.hip", "fa_bwd_tiles.hip"]
 
-# Per-source options. fa_bwd.hip: MFMAs in VGPR form (the d = 128 backward's
-# default AGPR form copies every S and dP result back for the vector math;
-# measured faster on the causal GQA backward, slower on the window one, which
-# lives in fa_bwd_window.hip).
+# Per-source options. fa_bwd.hip: MFMAs in VGPR form (kernels of more than
+# 256 registers per wave, the d = 128 dropout backward's, otherwise keep MFMA
+# results in AGPRs and copy every S and dP value back for the vector math).
 SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 ARCH = "gfx950"

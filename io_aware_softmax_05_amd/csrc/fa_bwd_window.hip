@@ -1,8 +1,10 @@
 // fa_bwd_window.hip -- backward pass launches for the causal sliding window.
 //
 // The kernels and their launch template are in fa_bwd_kernels.hpp; this file
-// is compiled with the compiler's default MFMA register form (measured faster
-// for these instantiations than the VGPR form fa_bwd.hip uses).
+// is compiled with the compiler's default MFMA register form. It measured
+// faster than the VGPR form fa_bwd.hip uses while the window ran the 32-key
+// dK/dV kernel; its kernels now stay within 256 registers, where the two
+// forms time the same.
 #include "fa_bwd_kernels.hpp"
 
 namespace fa {
