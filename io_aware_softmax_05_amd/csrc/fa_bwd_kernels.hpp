@@ -50,7 +50,7 @@ namespace {
 // small-GEMM interleave hint (iglp 0) ordering the LDS reads among the MFMAs;
 // d = 128: 4 waves (the dK/dV accumulators need up to 512 registers per
 // wave; 8 waves spill) and no hint. The launch picks other shapes per case
-// (non-causal d = 64 runs 4-wave workgroups of 32-row tiles, three per CU).
+// (non-causal d = 64 runs 4-wave workgroups of 32-row tiles).
 template <int D, int NW_ = (D == 64 ? 8 : 4), int BQ_ = 64, int NSTAGE_ = 2, int IGLP_ = (D == 64 ? 0 : -1),
           int OCC_ = 1>
 struct DkdvCfg {
@@ -1105,12 +1105,13 @@ using DqOneCfg = DqCfg<D, DqCfg<D>::NW, (D == 64 ? 32 : 64), (D == 64 ? 2 : 3), 
 
 template <int D, bool CAUSAL, bool WIN = false, bool DROP = false, bool ALT = false>
 static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
-  // non-causal d = 64: 4-wave workgroups, four per CU (measured on MI355X:
-  // GPT-2-shaped backward -1.3% on top of the dK/dV tiling below; the causal
-  // masked body spills in that shape and keeps 8 waves)
+  // non-causal d = 64, with or without dropout: 4-wave workgroups, four per
+  // CU (measured on MI355X: GPT-2-shaped backward -1.3% and its dropout form
+  // -1.6%, on top of the dK/dV tilings below; the causal masked body spills
+  // in that shape and keeps 8 waves)
+  using DQ64 = DqCfg<D, 4, 32, 2, -1, 4>;
   using QD = typename std::conditional<
-      DROP, DqOneCfg<D>,
-      typename std::conditional<D == 64 && !CAUSAL, DqCfg<D, 4, 32, 2, -1, 4>, DqCfg<D>>::type>::type;
+      D == 64 && !CAUSAL, DQ64, typename std::conditional<DROP, DqOneCfg<D>, DqCfg<D>>::type>::type;
   using QC = typename std::conditional<ALT, DqCfg<D, QD::NW, (QD::BC == 32 ? 64 : 32)>, QD>::type;
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + QC::BR - 1) / QC::BR;
@@ -1124,14 +1125,15 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   // two waves per SIMD; measured 27% faster on a causal T2048 layer)
   // causal d = 128 with dropout: 32-row tiles as well (the mask bytes push the
   // 64-row masked body past 512 registers)
-  // non-causal d = 64 without dropout: 4-wave workgroups of 32-row tiles at
-  // 150 registers, three per CU (three waves per SIMD; measured on MI355X:
-  // GPT-2-shaped backward -6% against one 8-wave workgroup of 64-row tiles)
+  // non-causal d = 64: 4-wave workgroups of 32-row tiles, three per CU at
+  // 150 registers without dropout, two per CU at 188 with it (measured on
+  // MI355X against one 8-wave workgroup of 64-row tiles: GPT-2-shaped
+  // backward -6%, its dropout form -3%; three per CU spilled with dropout)
   using KD = typename std::conditional<
       D == 64 && CAUSAL, DkdvCfg<D, 8, 32>,
-      typename std::conditional<DROP && CAUSAL, DkdvCfg<D, 4, 32>,
-                                typename std::conditional<D == 64 && !DROP, DkdvCfg<D, 4, 32, 2, 0, 3>,
-                                                          DkdvCfg<D>>::type>::type>::type;
+      typename std::conditional<
+          DROP && CAUSAL, DkdvCfg<D, 4, 32>,
+          typename std::conditional<D == 64, DkdvCfg<D, 4, 32, 2, 0, (DROP ? 2 : 3)>, DkdvCfg<D>>::type>::type>::type;
   // 16 keys per wave at d = 128, and for causal d = 64 (measured on MI355X:
   // causal GQA 32k backward -6%, its sliding-window form -22%, causal B64 H16
   // T1024 d64 -20%; the non-causal d = 64 layer timed the same with either
