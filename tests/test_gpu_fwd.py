@@ -83,6 +83,8 @@ BF16_SHAPES = [
     (1, 2, 2, 255, 64, 128, False),
     (1, 6, 2, 333, 333, 128, True),     # 3 query heads per KV head
     (2, 3, 3, 520, 520, 64, False),
+    (1, 2, 2, 700, 300, 128, True),     # Tq > Tk over several 256-row tiles: whole waves see no key
+    (1, 4, 2, 600, 1000, 128, True),    # Tq < Tk: every wave's diagonal lies past the first key tile
 ]
 
 
