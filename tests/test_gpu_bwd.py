@@ -40,7 +40,8 @@ BWD_SHAPES = [
     (2, 2, 1, 200, 129, 64, False),
     (1, 6, 2, 190, 190, 64, True),      # 3 query heads per KV head, ragged 64-row tiles
     (1, 6, 2, 300, 300, 128, False),
-    (1, 2, 2, 600, 600, 64, False),     # several 256-key workgroups and a ragged one
+    (1, 2, 2, 600, 600, 64, False),     # several 128-key workgroups and a ragged one
+    (1, 4, 2, 333, 517, 64, False),     # ragged 32-row query tiles and key tiles, Tq < Tk, GQA
     # causal walks that pair tile p with tile n - 1 - p (dK/dV over 128-key
     # tiles, dQ over query tiles): many pairs, an odd middle tile, Tq != Tk
     (1, 4, 2, 1152, 1152, 128, True),   # 9 key tiles, 9 query tiles: four pairs and a middle one

@@ -82,6 +82,7 @@ FWD_SHAPES = [
     (2, 4, 1, 100, 200, 128, True),     # Tq < Tk, 4 query heads per KV head
     (1, 2, 2, 150, 90, 64, True),       # Tq > Tk: the first 60 rows see no key
     (1, 6, 2, 190, 190, 64, True),
+    (1, 4, 2, 333, 517, 64, False),     # ragged 32-row query tiles of the 4-wave dK/dV, Tq < Tk
 ]
 
 
