@@ -637,10 +637,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv16_kernel(BwdArgs a, in
         dsw[rb][0] = pack_bf16x2(ds[0], ds[1]);
         dsw[rb][1] = pack_bf16x2(ds[2], ds[3]);
       }
-      // The compiler's interleave strategy 1 on the causal unmasked body
-      // (measured on MI355X: causal 32k GQA backward -4.5%; the non-causal
-      // instantiation ran 23% slower with it and takes none).
-      if constexpr (PAIR && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(1);
+      // The compiler's interleave strategy 1 on the unmasked body (measured on
+      // MI355X: causal 32k GQA backward -4.5%; with the operand reads issued
+      // ahead also the sliding-window backward -1..2% and the non-causal one
+      // -0.4..2.6%, which had run 23% slower with it before).
+      if constexpr (!decltype(masked)::value) __builtin_amdgcn_iglp_opt(1);
       // dV^T += dO^T P and dK^T += Q^T dS, 32 rows (blocks 2 hs and 2 hs + 1) per
       // step. Item i is (hs, db, dO^T or Q^T) = (i / (2 NDB), i / 2 % NDB, i % 2):
       // two transposed reads and one MFMA.
