@@ -1140,7 +1140,9 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   // T1024 d64 -20%; the non-causal d = 64 layer timed the same with either
   // layout and keeps the 32-key one)
   if constexpr (!DROP && !ALT && (D == 128 || CAUSAL)) {
-    using K16 = Dkdv16Cfg<D>;
+    // the sliding window takes a two-stage ring at d = 128 too (measured on
+    // MI355X: -2.3% against three stages; the causal layers are no faster so)
+    using K16 = Dkdv16Cfg<D, (WIN || D == 64) ? 2 : 3>;
     const int n_ktiles = (a.Tk + K16::BK - 1) / K16::BK;
     // causal without a window: one workgroup per pair of key tiles p, n - 1 - p
     const int n_units = CAUSAL && !WIN ? (n_ktiles + 1) / 2 : n_ktiles;
