@@ -15,8 +15,9 @@
 //     kv head (all query heads that share it) run on one XCD and its L2,
 //     query heads of a group side by side, causal tiles longest first.
 //     Causal: waves w and w + NW / 2 (one SIMD) take row blocks b and
-//     NW - 1 - b, and past the diagonal a wave skips the tiles none of its
-//     rows sees, so the SIMDs share that stretch evenly.
+//     NW - 1 - b, and past the diagonal (or, with a window, below the band)
+//     a wave skips the tiles none of its rows sees, so the SIMDs share those
+//     stretches evenly.
 //   * 64-key K and V tiles stream HBM -> registers -> LDS through buffer
 //     loads (out-of-range rows read as zeros, so the loop has no branches),
 //     double buffered with one barrier per tile. Row pitches are chosen for
@@ -136,17 +137,23 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
 
   // Causal: the two waves that share a SIMD (w and w + NW / 2) take row
   // blocks b and NW - 1 - b, so every SIMD has the same share of the tiles
-  // past the diagonal, which a wave skips once none of its rows sees them.
-  constexpr bool SKIP = CAUSAL && !WIN && !DROP;
+  // past the diagonal (and below a window), which a wave skips when none of
+  // its rows sees them.
+  constexpr bool SKIP = CAUSAL && !DROP;
   const int rblk = SKIP && wave >= C::NW / 2 ? C::NW - 1 - (wave - C::NW / 2) : wave;
   const int qrow = q0 + rblk * 32 + col;
-  // Tiles [0, w_full) are complete and visible to every row of this wave,
-  // tiles [w_end, n_kv) to none of them.
-  int w_full = n_full, w_end = n_kv;
+  // Tiles [w_head, w_full) are complete and visible to every row of this
+  // wave; tiles before w_begin (below every row's window) and from w_end on
+  // are visible to none of them.
+  int w_begin = j_begin, w_head = j_head, w_full = n_full, w_end = n_kv;
   if (SKIP) {
     const int r_first = q0 + rblk * 32 + shift;
     w_full = __builtin_amdgcn_readfirstlane(max(n_full, min(a.Tk / BC, max(0, r_first + 1) / BC)));
     w_end = __builtin_amdgcn_readfirstlane(min(n_kv, (min(a.Tk, max(0, r_first + 32)) + BC - 1) / BC));
+    if (WIN) {
+      w_begin = __builtin_amdgcn_readfirstlane(max(j_begin, min(n_kv, max(0, r_first - a.window + 1) / BC)));
+      w_head = __builtin_amdgcn_readfirstlane(min(j_head, max(w_begin, (max(0, r_first + 31 - a.window + 1) + BC - 1) / BC)));
+    }
   }
 
   // Q fragments: B operand of S^T = K Q^T (lane: query column, 8 dims).
@@ -278,8 +285,8 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
     load_k(j + 2);
     load_v(j + 1);
     // masked stretch: this wave's rows may see none of tile j or j + 1
-    const bool cur_live = !(SKIP && NM) || j < w_end;
-    const bool nxt_live = !(SKIP && NM) || j + 1 < w_end;
+    const bool cur_live = !(SKIP && NM) || (j < w_end && j >= w_begin);
+    const bool nxt_live = !(SKIP && NM) || (j + 1 < w_end && j + 1 >= w_begin);
     const float m_ref = (m == -INFINITY) ? 0.f : m;
     // stage A: S_{j+1} on the matrix cores, P_j = 2^(S_j c - m) on the vector unit
     if constexpr (HN) {
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
       float m_new = m;
       if (nxt_live) {
         if constexpr (NM) {
-          if (!SKIP || j + 1 >= w_full) mask(j + 1, s_nxt);
+          if (!SKIP || j + 1 >= w_full || (WIN && j + 1 < w_head)) mask(j + 1, s_nxt);
         }
         m_new = fmaxf(m, rowmax(s_nxt) * a.c);
       }
