@@ -21,7 +21,8 @@
 //     unrounded fp32 P', and O = v_scale * O' / l (the 2^5 cancels).
 //
 // gfx950 mapping (rows and tiles as in the bf16 forward: 32 queries per wave,
-// 64-key tiles, two-stage software pipeline, one barrier per tile)
+// 64-key tiles, two-stage software pipeline, one barrier per tile, and the
+// causal row-block pairing with per-wave skipping past the diagonal)
 //   * MFMA row m of 32-key block kb reads key row
 //     32 ((m >> 2) & 1) + 16 kb + 4 (m >> 3) + (m & 3) of the tile, so the S^T
 //     accumulator register r of lane half h holds key 32 h + 16 kb + r: each
@@ -114,7 +115,19 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
   n_full = min(n_full, n_kv - 1);
 
   // Q fragments (B operand of S^T): lane half h holds dims [64 ks + 32 h, +32).
-  const int qrow = q0 + wave * 32 + col;
+  // Causal: the two waves that share a SIMD (w and w + NW / 2) take row
+  // blocks b and NW - 1 - b, so every SIMD has the same share of the tiles
+  // past the diagonal, which a wave skips when none of its rows sees them.
+  const int rblk = CAUSAL && wave >= C::NW / 2 ? C::NW - 1 - (wave - C::NW / 2) : wave;
+  const int qrow = q0 + rblk * 32 + col;
+  // Tiles [0, w_full) are complete and visible to every row of this wave,
+  // tiles [w_end, n_kv) to none of them.
+  int w_full = n_full, w_end = n_kv;
+  if (CAUSAL) {
+    const int r_first = q0 + rblk * 32 + shift;
+    w_full = __builtin_amdgcn_readfirstlane(max(n_full, min(a.Tk / BC, max(0, r_first + 1) / BC)));
+    w_end = __builtin_amdgcn_readfirstlane(min(n_kv, (min(a.Tk, max(0, r_first + 32)) + BC - 1) / BC));
+  }
   i32x8 qf[KS];
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + qoff, (uint32_t)a.Tq * D);
@@ -217,34 +230,47 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 8 / Fp8Cfg<D>::NW) void fwd_fp8_kern
   // S_{j+1} goes to s_nxt, is masked if needed, and its row max moves m.
   auto body = [&](int j, auto next_masked, auto has_next, f32x16* s_cur, f32x16* s_nxt) {
     constexpr bool HN = decltype(has_next)::value;
+    constexpr bool NM = decltype(next_masked)::value;
     load_k(j + 2);
     load_v(j + 1);
+    // masked stretch: this wave's rows may see none of tile j or j + 1
+    const bool cur_live = !(CAUSAL && NM) || j < w_end;
+    const bool nxt_live = !(CAUSAL && NM) || j + 1 < w_end;
     const float neg_ref = kShift8 - ((m == -INFINITY) ? 0.f : m);
     // stage A: S_{j+1} on the matrix cores, P'_j on the vector unit
-    if constexpr (HN) scores((j + 1) & 1, s_nxt);
-    uint32_t pw[8];
+    if constexpr (HN) {
+      if (nxt_live) scores((j + 1) & 1, s_nxt);
+    }
     float lsum = 0.f;
+    if (cur_live) {
+      uint32_t pw[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const float p0 = exp2_fast(fmaf(s_cur[kb][r], c, neg_ref));
-        const float p1 = exp2_fast(fmaf(s_cur[kb][r + 1], c, neg_ref));
-        const float p2 = exp2_fast(fmaf(s_cur[kb][r + 2], c, neg_ref));
-        const float p3 = exp2_fast(fmaf(s_cur[kb][r + 3], c, neg_ref));
-        lsum += (p0 + p1) + (p2 + p3);
-        // bytes 16 kb + r .. +3 of this half: keys 32 half + 16 kb + r .. +3
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        pw[4 * kb + r / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-      }
-    const i32x8 pb = i32x8{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-    __builtin_amdgcn_iglp_opt(0);
-    // stage B: O'^T[d, query] += V^T[d, key] P'^T[key, query]
-    pv(j & 1, pb);
+        for (int r = 0; r < 16; r += 4) {
+          const float p0 = exp2_fast(fmaf(s_cur[kb][r], c, neg_ref));
+          const float p1 = exp2_fast(fmaf(s_cur[kb][r + 1], c, neg_ref));
+          const float p2 = exp2_fast(fmaf(s_cur[kb][r + 2], c, neg_ref));
+          const float p3 = exp2_fast(fmaf(s_cur[kb][r + 3], c, neg_ref));
+          lsum += (p0 + p1) + (p2 + p3);
+          // bytes 16 kb + r .. +3 of this half: keys 32 half + 16 kb + r .. +3
+          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          pw[4 * kb + r / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+        }
+      const i32x8 pb = i32x8{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+      __builtin_amdgcn_iglp_opt(0);
+      // stage B: O'^T[d, query] += V^T[d, key] P'^T[key, query]
+      pv(j & 1, pb);
+    }
     kahan_add(l, lc, lsum);
     if constexpr (HN) {
-      if constexpr (decltype(next_masked)::value) mask(j + 1, s_nxt);
-      const float m_new = fmaxf(m, rowmax(s_nxt) * c);
+      float m_new = m;
+      if (nxt_live) {
+        if constexpr (NM) {
+          if (!CAUSAL || j + 1 >= w_full) mask(j + 1, s_nxt);
+        }
+        m_new = fmaxf(m, rowmax(s_nxt) * c);
+      }
       const bool move = __builtin_amdgcn_ballot_w64(m_new > m + kSlack8) != 0;
       store_k(j & 1);
       store_v((j + 1) & 1);

@@ -104,6 +104,8 @@ FP8_SHAPES = [
     (1, 4, 2, 384, 384, 64, True),      # GQA, several diagonal tiles
     (1, 6, 2, 333, 336, 128, True),     # 3 query heads per kv head, ragged
     (1, 2, 2, 300, 128, 128, True),     # Tq > Tk: the first 172 rows see no key
+    (1, 2, 2, 700, 320, 128, True),     # Tq > Tk over several 256-row tiles: whole waves see no key
+    (1, 4, 2, 600, 1024, 128, True),    # Tq < Tk: every wave's diagonal past the first key tile
     (1, 2, 1, 100, 16, 64, False),      # a single 16-key chunk
 ]
 
