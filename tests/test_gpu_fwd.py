@@ -100,6 +100,30 @@ def test_bf16_parity(shape):
     gu.check_lse("LSE", lse, lse_ref, 1e-4)
 
 
+def _random_causal_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        out.append((1, hkv * int(rng.integers(1, 4)), hkv, int(rng.integers(1, 900)), int(rng.integers(1, 900)),
+                    int(rng.choice([64, 128])), True))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_causal_shapes(10, 31), ids=lambda s: "x".join(map(str, s)))
+def test_bf16_causal_random_shapes(shape):
+    """Seeded random causal (Tq, Tk, d, group) draws: the diagonal crosses the
+    row and key tiles anywhere, with Tq above and below Tk."""
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    print(f"[bf16 causal random {shape}]", flush=True)
+    hv, dev = gu.attention_case(3000 + Tq + Tk, B, Hq, Hkv, Tq, Tk, d)
+    scale = d ** -0.5
+    o, lse = _fwd(dev, True, scale)
+    o_r, lse_r = ref.attention_fwd(hv["q"], hv["k"], hv["v"], scale, True)
+    gu.check_bf16("O", o, o_r)
+    gu.check_lse("LSE", lse, lse_r, 1e-4)
+
+
 @pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
 def test_bf16_peaky_scores(d, causal):
     """Queries scaled by 8 give scores with sigma ~ 8, so the running maximum

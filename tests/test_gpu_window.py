@@ -47,6 +47,50 @@ def test_window_forward_parity(shape):
     gu.check_lse("LSE", lse, lse_r, 1e-4)
 
 
+def _random_window_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        g = int(rng.integers(1, 4))
+        out.append((1, hkv * g, hkv, int(rng.integers(1, 700)), int(rng.integers(1, 700)),
+                    int(rng.choice([64, 128])), int(rng.integers(1, 800))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_window_shapes(12, 2024), ids=lambda s: "x".join(map(str, s)))
+def test_window_forward_random_shapes(shape):
+    """Seeded random (Tq, Tk, W, d, group) draws: per-wave band edges land
+    anywhere inside the row and key tiles, including rows that see no key."""
+    B, Hq, Hkv, Tq, Tk, d, w = shape
+    print(f"[fwd window random {shape}]", flush=True)
+    hv, dev = gu.attention_case(900 + Tq + w, B, Hq, Hkv, Tq, Tk, d)
+    scale = d ** -0.5
+    o, lse = _fwd_window(dev, scale, w)
+    o_r, lse_r = ref.attention_fwd(hv["q"], hv["k"], hv["v"], scale, True, window=w)
+    gu.check_bf16("O", o, o_r)
+    gu.check_lse("LSE", lse, lse_r, 1e-4)
+
+
+@pytest.mark.parametrize("shape", _random_window_shapes(6, 77), ids=lambda s: "x".join(map(str, s)))
+def test_window_backward_random_shapes(shape):
+    B, Hq, Hkv, Tq, Tk, d, w = shape
+    print(f"[bwd window random {shape}]", flush=True)
+    hv, dev = gu.attention_case(1100 + Tq + w, B, Hq, Hkv, Tq, Tk, d, with_dout=True)
+    scale = d ** -0.5
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = _fwd_window(dev, scale, w)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Tq, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    fa.fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, Tq, Tk, d, scale, w)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = ref.attention_bwd(hv["q"], hv["k"], hv["v"], hv["do"], scale, True, window=w)
+    gu.check_bf16("dQ", dq, dq_r)
+    gu.check_bf16("dK", dk, dk_r)
+    gu.check_bf16("dV", dv, dv_r)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_window_as_long_as_the_sequence_is_the_causal_kernel(d):
     """A window covering every row's keys computes exactly what the causal
