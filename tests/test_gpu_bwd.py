@@ -64,6 +64,31 @@ def test_bwd_parity(shape):
     gu.check_bf16("dV", dv, dv_r)
 
 
+def _random_bwd_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        out.append((1, hkv * int(rng.integers(1, 4)), hkv, int(rng.integers(1, 800)), int(rng.integers(1, 800)),
+                    int(rng.choice([64, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_bwd_shapes(10, 5), ids=lambda s: "x".join(map(str, s)))
+def test_bwd_random_shapes(shape):
+    """Seeded random draws over Tq, Tk, d, the group size and the mask: the
+    paired causal walks, the diagonal and the ragged tiles land anywhere."""
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    print(f"[bwd random {shape}]", flush=True)
+    hv, dev = gu.attention_case(5000 + Tq + Tk, B, Hq, Hkv, Tq, Tk, d, with_dout=True)
+    scale = d ** -0.5
+    dq, dk, dv = _fwd_bwd(dev, causal, scale)
+    dq_r, dk_r, dv_r = ref.attention_bwd(hv["q"], hv["k"], hv["v"], hv["do"], scale, causal)
+    gu.check_bf16("dQ", dq, dq_r)
+    gu.check_bf16("dK", dk, dk_r)
+    gu.check_bf16("dV", dv, dv_r)
+
+
 def _storage_allowance(hv, scale, causal):
     """First-order error that bf16 storage of O, P and dS can cause, per
     output element (unit roundoff u = 2^-8).
