@@ -106,6 +106,36 @@ def test_dropout_fwd_bwd_parity(shape, p_drop):
     gu.check_bf16("dV", dv, dv_r)
 
 
+def _random_dropout_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        out.append((1, hkv * int(rng.integers(1, 4)), hkv, int(rng.integers(1, 500)), int(rng.integers(1, 500)),
+                    int(rng.choice([64, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_dropout_shapes(6, 13), ids=lambda s: "x".join(map(str, s)))
+def test_dropout_random_shapes(shape):
+    """Seeded random draws over Tq, Tk, d, the group size and the mask, p = 0.2."""
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    print(f"[dropout random {shape}]", flush=True)
+    hv, dev = gu.attention_case(1700 + Tq + Tk, B, Hq, Hkv, Tq, Tk, d, with_dout=True)
+    scale = d ** -0.5
+    drop = ref.Dropout(t=fa.fa_dropout_keep_threshold(0.2), seed=SEED, offset=OFFSET)
+    o, lse = _fwd(dev, causal, scale, 0.2)
+    dq, dk, dv = _bwd(dev, o, lse, causal, scale, 0.2)
+    torch.cuda.synchronize()
+    o_r, lse_r = ref.attention_fwd(hv["q"], hv["k"], hv["v"], scale, causal, dropout=drop)
+    gu.check_bf16("O", o, o_r)
+    gu.check_lse("LSE", lse, lse_r, 1e-4)
+    dq_r, dk_r, dv_r = ref.attention_bwd(hv["q"], hv["k"], hv["v"], hv["do"], scale, causal, dropout=drop)
+    gu.check_bf16("dQ", dq, dq_r)
+    gu.check_bf16("dK", dk, dk_r)
+    gu.check_bf16("dV", dv, dv_r)
+
+
 def test_dropout_zero_is_the_plain_pass():
     hv, dev = gu.attention_case(41, 1, 2, 2, 200, 200, 64, with_dout=True)
     o0 = torch.empty_like(dev["q"])

@@ -123,6 +123,27 @@ def test_fp8_forward_parity(shape):
         assert np.all(og[:, :, :Tq - Tk] == 0) and np.all(lg[:, :, :Tq - Tk] == -np.inf)
 
 
+def _random_fp8_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        out.append((1, hkv * int(rng.integers(1, 4)), hkv, int(rng.integers(1, 700)), 16 * int(rng.integers(1, 45)),
+                    int(rng.choice([64, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_fp8_shapes(8, 11), ids=lambda s: "x".join(map(str, s)))
+def test_fp8_forward_random_shapes(shape):
+    """Seeded random draws (Tk a multiple of 16, as the entry point requires)."""
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    print(f"[fp8 fwd random {shape}]", flush=True)
+    x = inputs.draw_fp8_attention_inputs(1300 + Tq + Tk, B, Hq, Hkv, Tq, Tk, d)
+    scale = d ** -0.5
+    o, lse = _run(x, scale, causal)
+    _check(x, o, lse, scale, causal)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp8_peaky_scores_move_the_reference(d):
     # scale x8: scores spread over many powers of two, so the reference max
