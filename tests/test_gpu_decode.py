@@ -51,6 +51,34 @@ def test_decode_parity(shape, chunk):
     gu.check_lse("LSE", lse, lse_ref, 1e-4)
 
 
+def _random_decode_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 5))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+        t_max = int(rng.integers(1, 3000))
+        lo = int(rng.integers(1, t_max + 1))
+        out.append((int(rng.integers(1, 5)), hkv * g, hkv, t_max, int(rng.choice([64, 128])), lo, t_max,
+                    int(rng.choice([0, 64, 256, 1024]))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_decode_shapes(10, 17), ids=lambda s: "x".join(map(str, s)))
+def test_decode_random_shapes(shape):
+    """Seeded random draws over batch, group size (up to a full 16-row MFMA),
+    cache length, length spread, d and the chunk size."""
+    B, Hq, Hkv, Tk_max, d, lo, hi, chunk = shape
+    print(f"[decode random {shape}]", flush=True)
+    raw, dev, lens = _case(2100 + Tk_max, B, Hq, Hkv, Tk_max, d, lo, hi)
+    scale = d ** -0.5
+    o, lse = _decode(dev, lens, scale, chunk)
+    o_ref, lse_ref = ref.decode(inputs.widen(raw["q"]), inputs.widen(raw["k"]), inputs.widen(raw["v"]),
+                                raw["seq_lens"], scale)
+    gu.check_bf16("O", o, o_ref)
+    gu.check_lse("LSE", lse, lse_ref, 1e-4)
+
+
 def test_decode_matches_fwd_one_query():
     """Decoding equals the forward pass with one query row over the first L keys."""
     raw, dev, lens = _case(3, 2, 8, 2, 500, 128, 200, 500)
