@@ -302,8 +302,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int n_ro
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
+  static_assert(PER == 1 || PER == 2, "head width");
   __shared__ float red_m[4];
-  __shared__ float red_u[4][D + 1];
+  // one row per wave: its D partial sums (written and read as PER-float
+  // vectors, so the lanes' accesses fall on distinct banks) and its l
+  __shared__ __attribute__((aligned(16))) float red_u[4][D + 4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq;
@@ -339,18 +342,29 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, u[e], acc[e]);
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) red_u[wave][lane * PER + e] = acc[e];
+  if constexpr (PER == 2) {
+    *(float2*)&red_u[wave][lane * 2] = float2{acc[0], acc[PER - 1]};
+  } else {
+    red_u[wave][lane] = acc[0];
+  }
   if (lane == 0) red_u[wave][D] = lsum - lcomp;
   __syncthreads();
   if (wave != 0) return;
   const float l_tot = red_u[0][D] + red_u[1][D] + red_u[2][D] + red_u[3][D];
   const float inv = 1.f / l_tot;
   float o[PER];
+  if constexpr (PER == 2) {
+    float2 t = *(const float2*)&red_u[0][lane * 2];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int c = lane * PER + e;
-    o[e] = (red_u[0][c] + red_u[1][c] + red_u[2][c] + red_u[3][c]) * inv;
+    for (int w = 1; w < 4; ++w) {
+      const float2 x = *(const float2*)&red_u[w][lane * 2];
+      t.x += x.x;
+      t.y += x.y;
+    }
+    o[0] = t.x * inv;
+    o[PER - 1] = t.y * inv;
+  } else {
+    o[0] = (red_u[0][lane] + red_u[1][lane] + red_u[2][lane] + red_u[3][lane]) * inv;
   }
   if (PER == 2) {
     *(uint32_t*)dst = pack_bf16x2(o[0], o[PER - 1]);
