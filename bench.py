@@ -585,7 +585,7 @@ def cpu_baseline(raw, full=False):
         r2, w2 = raw[2], INPUT_WORKLOADS[2]
         jobs = [("fwdbwd", r2["q"][b, h], r2["k"][b, h], r2["v"][b, h], r2["do"][b, h], w2.scale, False)
                 for b in range(w2.B) for h in range(w2.Hq)]
-        walls = [_pool_wall(pool, jobs) for _ in range(3 if full else 1)]
+        walls = [_pool_wall(pool, jobs) for _ in range(3)]
         flop2 = 3.5 * fwd_flops(w2.B, w2.Hq, w2.Tq, w2.Tk, w2.d, False)
         cfg[w2.name] = {"median_s": round(float(np.median(walls)), 3), "passes": len(walls),
                         "TFLOP/s": round(flop2 / float(np.median(walls)) / 1e12, 5), "whole_workload": True}
@@ -865,8 +865,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-full", action="store_true",
-                    help="oracle baseline with the GPT-2-medium layer in 3 passes and the 32k GQA layer's fwd+bwd "
-                         "for KV groups 0 and 7 in full (minutes of CPU time)")
+                    help="oracle baseline with the 32k GQA layer's fwd+bwd for KV groups 0 and 7 in full "
+                         "(minutes of CPU time)")
     ap.add_argument("--no-extras", action="store_true", help="headline only")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the amd-smi clock reading (profiled runs: a profiler loaded into every child "
