@@ -34,8 +34,8 @@
 //   * Two-stage software pipeline per key tile j: stage A issues the MFMAs
 //     of S_{j+1} = K_{j+1} Q^T while the vector unit turns S_j into
 //     probabilities; stage B issues O += V_j P_j while the vector unit takes
-//     the row maximum of S_{j+1}. The compiler's MFMA/exp interleave strategy
-//     (iglp 2) orders the instructions of each stage.
+//     the row maximum of S_{j+1}. A compiler interleave strategy orders the
+//     instructions of each stage (small-GEMM at d = 128, MFMA/exp at d = 64).
 //   * The running maximum is only moved when some row of the wave grows by
 //     more than 2^8; otherwise the stale maximum is kept, the probabilities
 //     stay below 256 and l and u need no rescale (the result is the same up
@@ -317,7 +317,9 @@ __global__ __launch_bounds__(C::NT, 8 / C::NW) void fwd_bf16_kernel(FwdArgs a) {
           pb[kb_i * 2 + hs] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
         }
       }
-      __builtin_amdgcn_iglp_opt(2);
+      // the compiler's interleave strategy: the small-GEMM one (0) at d = 128,
+      // the MFMA/exp one (2) at d = 64 (each measured fastest on MI355X there)
+      __builtin_amdgcn_iglp_opt(D == 128 ? 0 : 2);
       // stage B: O^T[d, query] += V^T[d, key] P^T[key, query], 16 keys per step
       const FA_LDS uint8_t* vb = vbuf + (j & 1) * VTILE + v_rd;
 #pragma unroll
