@@ -87,9 +87,9 @@ TRAFFIC_UNITS = {
     "fa_fwd B64 H16 T1024 d64": ["fwd_bf16_kernel<64, false, false, false>"],
     "fa_bwd B64 H16 T1024 d64": ["bwd_dq_kernel<64, false, false, false>", "bwd_dkdv_kernel<64, false, false, false>"],
     # the causal 8k and 32k forwards run the same kernel: told apart by grid size (threads)
-    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true, false, false>@524288"],
+    "fa_fwd causal B1 H32 T8192 d128": ["fwd_bf16_kernel<128, true, false, false>@262144"],
     "fa_decode_splitkv B16 Hq32 Hkv8 d128": ["decode_split_kernel<128, 3>", "decode_merge_kernel<128>"],
-    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false, false>@2097152"],
+    "fa_fwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["fwd_bf16_kernel<128, true, false, false>@1048576"],
     "fa_bwd causal GQA B1 Hq32 Hkv8 T32768 d128": ["bwd_dq_kernel<128, true, false, false>",
                                                    "bwd_dkdv16_kernel<128, true, false>"],
     "fa_fwd_window B1 Hq32 Hkv8 T32768 W4096 d128": ["fwd_bf16_kernel<128, true, true, false>"],
