@@ -104,290 +104,309 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dkdv_kernel(BwdArgs a, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
+  // Causal without a window, a workgroup takes key tiles p and n - 1 - p, one
+  // after the other (the same number of query tiles for every workgroup);
+  // otherwise one key tile.
+  constexpr bool PAIRK = CAUSAL && !WIN;
+  const int n_units = PAIRK ? (n_ktiles + 1) / 2 : n_ktiles;
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = (int)(t % (uint32_t)n_ktiles);   // causal: small kt has the most work
-  const int bhk = (int)(t / (uint32_t)n_ktiles);
+  const int unit = (int)(t % (uint32_t)n_units);
+  const int bhk = (int)(t / (uint32_t)n_units);
   const int b = bhk / a.Hkv, hk = bhk - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int k0 = kt * C::BK;
-  const int kw0 = k0 + wave * 32;                 // first key of this wave
-  const int key = kw0 + col;                      // this lane's key
-  const int shift = a.Tk - a.Tq;
-  const size_t kvoff = (size_t)bhk * a.Tk * D;
 
-  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
-    const uint32_t base = key < a.Tk ? (uint32_t)(key * D + 8 * half) * 2 : kOutOfRange;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kf[ks] = as_bf16x8(buf_load_b128(krs, base + ks * 32));
-      vf[ks] = as_bf16x8(buf_load_b128(vrs, base + ks * 32));
-    }
-  }
+  // One key tile kt of this workgroup.
+  auto key_tile = [&](const int kt) __attribute__((always_inline)) {
+    const int k0 = kt * C::BK;
+    const int kw0 = k0 + wave * 32;                 // first key of this wave
+    const int key = kw0 + col;                      // this lane's key
+    const int shift = a.Tk - a.Tq;
+    const size_t kvoff = (size_t)bhk * a.Tk * D;
 
-  f32x16 dv_acc[D / 32], dk_acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dv_acc[db][r] = 0.f;
-      dk_acc[db][r] = 0.f;
-    }
-
-  // Query tiles that can see any key of this workgroup, for each query head of the group.
-  int qt_begin = 0;
-  if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
-  int n_qt = (a.Tq + BQ - 1) / BQ;
-  if (WIN) {   // rows past the last key's window see none of these keys
-    const int last_row = k0 + C::BK - 1 - shift + a.window - 1;
-    n_qt = last_row < 0 ? 0 : min(n_qt, last_row / BQ + 1);
-  }
-  const int per_head = max(0, n_qt - qt_begin);
-  const int n_iter = per_head * G;
-
-  // This thread's share of the tile loads: physical chunk p of the tile holds
-  // logical chunk p ^ swz(row) of its row.
-  uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
-  bool dma_is_do[C::DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const int n = wave * C::DMA_PER_WAVE + i;
-    const int m = n % (C::TILE_DMA / 2);
-    dma_is_do[i] = n >= C::TILE_DMA / 2;
-    const int p = 64 * m + lane;
-    const int r = p / CH, pc = p % CH;
-    dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
-    dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
-  }
-  const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
-
-  // Iteration order. The workgroups resident on one XCD hold consecutive key
-  // tiles of one KV head.
-  //   * Without a window: query tiles from the last one down to the first
-  //     that sees this workgroup's keys, every query head of the group per
-  //     tile. The resident workgroups start on the same (tile, head) and walk
-  //     in step, so each Q/dO tile they read is fetched once into the XCD's L2.
-  //   * With a window each workgroup sees only a band of about W / BQ tiles
-  //     that starts at its diagonal: the heads are outermost and the tiles go
-  //     up from the diagonal, so a neighbour reads the same tile two steps
-  //     later, while it is still in L2.
-  // DOWN is the first order. Tile iterator for the loads (ahead of the compute):
-  constexpr bool DOWN = !WIN;
-  int ld_it = 0, ld_h = 0, ld_qi = DOWN ? n_qt - 1 : qt_begin;
-  // Rows past Tq lie past the end of the buffer ranges and read as zeros, so
-  // only an exhausted iterator needs an out-of-range base.
-  auto issue = [&](auto stage_c) FA_INLINE {
-    FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
-    const bool live = ld_it < n_iter;
-    const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
-    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.stats + rows, (uint32_t)a.Tq * 4);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.stats + plane + rows, (uint32_t)a.Tq * 4);
-    const uint32_t tbase = live ? (uint32_t)(ld_qi * BQ) * D * 2 : kOutOfRange;
-    const uint32_t sbase = live ? (uint32_t)(ld_qi * BQ) * 4 : kOutOfRange;
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], tbase + dma_off[i]);
-#pragma unroll
-    for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
-      // lanes past BQ rows (BQ < 64) fill unread bytes of the slot
-      constexpr int PER_PLANE = C::STAT_DMA / 2;
-      const int pl = i / PER_PLANE, row = 64 * (i % PER_PLANE) + lane;
-      dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE), sbase + (uint32_t)row * 4);
-    }
-    ++ld_it;
-    if constexpr (DOWN) {
-      if (++ld_h == G) {
-        ld_h = 0;
-        if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
-      }
-    } else if (++ld_qi == n_qt) {
-      ld_qi = qt_begin;
-      if (ld_h + 1 < G) ++ld_h;          // past the last head: loads read zeros (live is false)
-    }
-  };
-
-  // LDS read offsets (bytes inside a tile).
-  const uint32_t fq = swz<D>(col);
-  const uint32_t q_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
-  const int grp = lane >> 4, gi = lane & 15;
-  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
-  const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
-  const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
-  const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
-  const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
-
-  FA_LDS uint8_t* ztile = smem + C::NSTAGE * STAGE + wave * ZTILE;
-
-  auto body = [&](const FA_LDS uint8_t* st, int q0, int head, auto masked) FA_INLINE {
-    const FA_LDS uint8_t* qt = st;
-    const FA_LDS uint8_t* gt = st + QTILE;
-    const FA_LDS uint8_t* stt = st + 2 * QTILE;
-    const uint32_t bhq = (uint32_t)(b * a.Hq + hk * G + head);   // flattened query head (dropout stream)
-    // S = Q K^T and dP = dO V^T for BQ queries x 32 keys (one key per lane).
-    // On unmasked tiles without dropout the dP product starts from -D
-    // (accumulator register r of block qb holds row 32 qb + 8 (r / 4) +
-    // 4 half + r % 4, so four -D values of consecutive rows fill registers
-    // 4 g4 .. 4 g4 + 3), and dP - D comes out of the matrix cores; masked
-    // tiles (fewer, and short of registers) and dropout add -D afterwards.
-    constexpr bool FOLD = !DROP && !decltype(masked)::value;
-    f32x16 s[QB], dp[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 dinit{};
-      if constexpr (FOLD) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 nd = *(const FA_LDS f32x4*)(stt + C::SLOT + (qb * 32 + 8 * g4 + 4 * half) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dinit[4 * g4 + e] = nd[e];
-        }
-      }
-#pragma unroll
+    // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + kvoff, (uint32_t)a.Tk * D * 2);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + kvoff, (uint32_t)a.Tk * D * 2);
+      const uint32_t base = key < a.Tk ? (uint32_t)(key * D + 8 * half) * 2 : kOutOfRange;
+  #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const uint32_t off = qb * 32 * ROWB + (q_rd ^ (32 * ks));
-        // the first products start from an inline zero (no register clearing) or from -D
-        s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], ks == 0 ? f32x16{} : s[qb]);
-        dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? dinit : dp[qb]);
+        kf[ks] = as_bf16x8(buf_load_b128(krs, base + ks * 32));
+        vf[ks] = as_bf16x8(buf_load_b128(vrs, base + ks * 32));
       }
     }
-    // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
-    // Masked tiles: row q0 + 32 qb + 8 g4 + 4 half + e sees this lane's key iff
-    // 0 <= dist < window with dist = (that row + shift - key) = dbase + 32 qb + 8 g4 + e.
-    const int dbase = q0 + 4 * half + shift - key;
-    uint32_t pw[QB][8], dsw[QB][8];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // Dropout bytes for (row 32 qb + 8 g4 + 4 half + e, this lane's key), in
-      // register order 4 g4 + e. Lane (c, h) draws row 32 qb + c's bytes for
-      // the 16 keys kw0 + 16 h .. +15 (the forward's Philox contract), stores
-      // them row-major in the wave's tile and reads back its own key column.
-      uint32_t zbyte[16];
-      if constexpr (DROP) {
-        const u32x4 w = philox4x32_10<false>((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
-                                      a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
-        lds_write_b128(ztile, col * ZPITCH + 16 * half, w);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) zbyte[i] = ztile[(8 * (i >> 2) + 4 * half + (i & 3)) * ZPITCH + col];
-      }
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int rq = qb * 32 + 8 * g4 + 4 * half;
-        const f32x4 l2 = *(const FA_LDS f32x4*)(stt + rq * 4);   // lse2 of rows rq .. rq + 3
-        f32x4 nd{};                                               // their -D, unless folded into dP
-        if constexpr (!FOLD) nd = *(const FA_LDS f32x4*)(stt + C::SLOT + rq * 4);
-        float p[4], ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
-          if constexpr (decltype(masked)::value) {
-            const int dist = dbase + (qb * 32 + 8 * g4 + e);   // one unsigned compare for the band
-            if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
-          }
-          float dpe = dp[qb][r];   // dP - D when folded, else dP
-          float pv = pe;
-          if constexpr (DROP) {   // dV takes the kept P; dP is dropped and rescaled
-            const bool keep = zbyte[r] < a.drop.t;
-            pv = keep ? pe : 0.f;
-            dpe = keep ? dpe * a.drop.inv_keep : 0.f;
-          }
-          if constexpr (!FOLD) dpe += nd[e];
-          p[e] = pv;
-          ds[e] = pe * dpe;
-        }
-        pw[qb][2 * g4] = pack_bf16x2(p[0], p[1]);
-        pw[qb][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
-        dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
-        dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
-      }
-    }
-    // (the hint on the unmasked body only: on the masked one it costs registers)
-    if constexpr (C::IGLP >= 0 && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(C::IGLP);
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 pb = as_bf16x8(u32x4{pw[qb][4 * hs], pw[qb][4 * hs + 1], pw[qb][4 * hs + 2], pw[qb][4 * hs + 3]});
-        const bf16x8 sb = as_bf16x8(u32x4{dsw[qb][4 * hs], dsw[qb][4 * hs + 1], dsw[qb][4 * hs + 2], dsw[qb][4 * hs + 3]});
-        const uint32_t hb = (qb * 32 + hs * 16) * ROWB;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const u32x2 glo = lds_read_tr(gt, hb + (tr_lo ^ (64 * db)));
-          const u32x2 ghi = lds_read_tr(gt, hb + (tr_hi ^ (64 * db)));
-          dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
-          const u32x2 qlo = lds_read_tr(qt, hb + (tr_lo ^ (64 * db)));
-          const u32x2 qhi = lds_read_tr(qt, hb + (tr_hi ^ (64 * db)));
-          dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
-        }
-      }
-  };
 
-  // Ring of NSTAGE tiles, NSTAGE - 1 loads ahead of the compute. The loop is
-  // unrolled NSTAGE times, so every stage is a compile-time LDS offset.
-  constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::VM_PER_TILE;
-  if (n_iter > 0) {
-    static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(st); });
-    wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
-  }
-  int cur_qi = DOWN ? n_qt - 1 : qt_begin, cur_h = 0;
-  auto step = [&](auto stage_c, auto may_mask) FA_INLINE {
-    constexpr int CS = decltype(stage_c)::value;
-    issue(std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});   // zeros past the end
-    const FA_LDS uint8_t* st = smem + CS * STAGE;
-    const int q0 = cur_qi * BQ;
-    // some (row, key) pair of this wave is masked (causal limit or window start)
-    if (decltype(may_mask)::value &&
-        ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0)))
-      body(st, q0, cur_h, std::true_type{});
-    else
-      body(st, q0, cur_h, std::false_type{});
-    wait_vm_barrier<AHEAD_VM>();          // the next tile has landed; this stage is free
-    if constexpr (DOWN) {
-      if (++cur_h == G) {
-        cur_h = 0;
-        --cur_qi;
-      }
-    } else if (++cur_qi == n_qt) {
-      cur_qi = qt_begin;
-      ++cur_h;
-    }
-  };
-  int it = 0;
-  if constexpr (CAUSAL && !WIN) {
-    // tiles whose first row sees every key of the workgroup need no mask; the
-    // downward walk visits them first (whole groups of NSTAGE iterations)
-    const int qi_full = (k0 + C::BK - 1 - shift + BQ - 1) / BQ;   // first tile with no masked pair
-    const int it_full = max(0, n_qt - max(qi_full, qt_begin)) * G / C::NSTAGE * C::NSTAGE;
-    for (; it < it_full; it += C::NSTAGE)
-      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(s, std::false_type{}); });
-  }
-  for (; it < n_iter; it += C::NSTAGE)
-    static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
-      if (it + decltype(s)::value < n_iter) step(s, std::true_type{});
-    });
-  if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
-
-  if (key < a.Tk) {
-    uint16_t* dkp = a.dk + kvoff + (size_t)key * D;
-    uint16_t* dvp = a.dv + kvoff + (size_t)key * D;
-#pragma unroll
+    f32x16 dv_acc[D / 32], dk_acc[D / 32];
+  #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        const f32x16& kk = dk_acc[db];
-        const f32x16& vv = dv_acc[db];
-        *(u32x2*)(dkp + d0) = u32x2{pack_bf16x2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale),
-                                    pack_bf16x2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale)};
-        const float sv = DROP ? a.drop.inv_keep : 1.f;   // dV = (P Z)^T dO * 256 / t
-        *(u32x2*)(dvp + d0) = u32x2{pack_bf16x2(vv[4 * g4] * sv, vv[4 * g4 + 1] * sv),
-                                    pack_bf16x2(vv[4 * g4 + 2] * sv, vv[4 * g4 + 3] * sv)};
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dv_acc[db][r] = 0.f;
+        dk_acc[db][r] = 0.f;
       }
+
+    // Query tiles that can see any key of this workgroup, for each query head of the group.
+    int qt_begin = 0;
+    if (CAUSAL) qt_begin = max(0, k0 - shift) / BQ;
+    int n_qt = (a.Tq + BQ - 1) / BQ;
+    if (WIN) {   // rows past the last key's window see none of these keys
+      const int last_row = k0 + C::BK - 1 - shift + a.window - 1;
+      n_qt = last_row < 0 ? 0 : min(n_qt, last_row / BQ + 1);
+    }
+    const int per_head = max(0, n_qt - qt_begin);
+    const int n_iter = per_head * G;
+
+    // This thread's share of the tile loads: physical chunk p of the tile holds
+    // logical chunk p ^ swz(row) of its row.
+    uint32_t dma_off[C::DMA_PER_WAVE], dma_dst[C::DMA_PER_WAVE];
+    bool dma_is_do[C::DMA_PER_WAVE];
+  #pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int n = wave * C::DMA_PER_WAVE + i;
+      const int m = n % (C::TILE_DMA / 2);
+      dma_is_do[i] = n >= C::TILE_DMA / 2;
+      const int p = 64 * m + lane;
+      const int r = p / CH, pc = p % CH;
+      dma_off[i] = (uint32_t)(r * D + (pc ^ swz<D>(r)) * 8) * 2;
+      dma_dst[i] = (dma_is_do[i] ? QTILE : 0) + m * 1024;
+    }
+    const size_t plane = (size_t)a.B * a.Hq * a.Tq;   // -D plane of the statistics workspace
+
+    // Iteration order. The workgroups resident on one XCD hold consecutive key
+    // tiles of one KV head.
+    //   * Without a window: query tiles from the last one down to the first
+    //     that sees this workgroup's keys, every query head of the group per
+    //     tile. The resident workgroups start on the same (tile, head) and walk
+    //     in step, so each Q/dO tile they read is fetched once into the XCD's L2.
+    //   * With a window each workgroup sees only a band of about W / BQ tiles
+    //     that starts at its diagonal: the heads are outermost and the tiles go
+    //     up from the diagonal, so a neighbour reads the same tile two steps
+    //     later, while it is still in L2.
+    // DOWN is the first order. Tile iterator for the loads (ahead of the compute):
+    constexpr bool DOWN = !WIN;
+    int ld_it = 0, ld_h = 0, ld_qi = DOWN ? n_qt - 1 : qt_begin;
+    // Rows past Tq lie past the end of the buffer ranges and read as zeros, so
+    // only an exhausted iterator needs an out-of-range base.
+    auto issue = [&](auto stage_c) FA_INLINE {
+      FA_LDS uint8_t* st = smem + decltype(stage_c)::value * STAGE;
+      const bool live = ld_it < n_iter;
+      const size_t rows = ((size_t)b * a.Hq + (size_t)(hk * G + (live ? ld_h : 0))) * a.Tq;
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + rows * D, (uint32_t)a.Tq * D * 2);
+      const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + rows * D, (uint32_t)a.Tq * D * 2);
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.stats + rows, (uint32_t)a.Tq * 4);
+      const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.stats + plane + rows, (uint32_t)a.Tq * 4);
+      const uint32_t tbase = live ? (uint32_t)(ld_qi * BQ) * D * 2 : kOutOfRange;
+      const uint32_t sbase = live ? (uint32_t)(ld_qi * BQ) * 4 : kOutOfRange;
+  #pragma unroll
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_b128(dma_is_do[i] ? grs : qrs, st + dma_dst[i], tbase + dma_off[i]);
+  #pragma unroll
+      for (int i = 0; i < C::STAT_DMA; ++i) {   // every wave loads them (same bytes, same place)
+        // lanes past BQ rows (BQ < 64) fill unread bytes of the slot
+        constexpr int PER_PLANE = C::STAT_DMA / 2;
+        const int pl = i / PER_PLANE, row = 64 * (i % PER_PLANE) + lane;
+        dma_b32(pl ? drs : lrs, st + 2 * QTILE + pl * C::SLOT + 256 * (i % PER_PLANE), sbase + (uint32_t)row * 4);
+      }
+      ++ld_it;
+      if constexpr (DOWN) {
+        if (++ld_h == G) {
+          ld_h = 0;
+          if (ld_qi > qt_begin) --ld_qi;   // past the last tile: loads read zeros (live is false)
+        }
+      } else if (++ld_qi == n_qt) {
+        ld_qi = qt_begin;
+        if (ld_h + 1 < G) ++ld_h;          // past the last head: loads read zeros (live is false)
+      }
+    };
+
+    // LDS read offsets (bytes inside a tile).
+    const uint32_t fq = swz<D>(col);
+    const uint32_t q_rd = col * ROWB + 16 * (half ^ (fq & 1)) + 32 * (fq >> 1);   // ^ 32 ks
+    const int grp = lane >> 4, gi = lane & 15;
+    const int tr_row = 4 * (grp >> 1) + (gi >> 2);
+    const uint32_t low2 = 2 * (grp & 1) + ((gi >> 1) & 1);
+    const uint32_t f_lo = swz<D>(tr_row), f_hi = swz<D>(tr_row + 8);
+    const uint32_t tr_lo = tr_row * ROWB + 64 * (f_lo >> 2) + 16 * (low2 ^ (f_lo & 3)) + 8 * (gi & 1);        // ^ 64 db
+    const uint32_t tr_hi = (tr_row + 8) * ROWB + 64 * (f_hi >> 2) + 16 * (low2 ^ (f_hi & 3)) + 8 * (gi & 1);
+
+    FA_LDS uint8_t* ztile = smem + C::NSTAGE * STAGE + wave * ZTILE;
+
+    auto body = [&](const FA_LDS uint8_t* st, int q0, int head, auto masked) FA_INLINE {
+      const FA_LDS uint8_t* qt = st;
+      const FA_LDS uint8_t* gt = st + QTILE;
+      const FA_LDS uint8_t* stt = st + 2 * QTILE;
+      const uint32_t bhq = (uint32_t)(b * a.Hq + hk * G + head);   // flattened query head (dropout stream)
+      // S = Q K^T and dP = dO V^T for BQ queries x 32 keys (one key per lane).
+      // On unmasked tiles without dropout the dP product starts from -D
+      // (accumulator register r of block qb holds row 32 qb + 8 (r / 4) +
+      // 4 half + r % 4, so four -D values of consecutive rows fill registers
+      // 4 g4 .. 4 g4 + 3), and dP - D comes out of the matrix cores; masked
+      // tiles (fewer, and short of registers) and dropout add -D afterwards.
+      constexpr bool FOLD = !DROP && !decltype(masked)::value;
+      f32x16 s[QB], dp[QB];
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 dinit{};
+        if constexpr (FOLD) {
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 nd = *(const FA_LDS f32x4*)(stt + C::SLOT + (qb * 32 + 8 * g4 + 4 * half) * 4);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) dinit[4 * g4 + e] = nd[e];
+          }
+        }
+  #pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const uint32_t off = qb * 32 * ROWB + (q_rd ^ (32 * ks));
+          // the first products start from an inline zero (no register clearing) or from -D
+          s[qb] = mfma32(as_bf16x8(lds_read_b128(qt, off)), kf[ks], ks == 0 ? f32x16{} : s[qb]);
+          dp[qb] = mfma32(as_bf16x8(lds_read_b128(gt, off)), vf[ks], ks == 0 ? dinit : dp[qb]);
+        }
+      }
+      // P and dS, packed to bf16 in the accumulator order (rows 32 qb + 8 g4 + 4 half + e).
+      // Masked tiles: row q0 + 32 qb + 8 g4 + 4 half + e sees this lane's key iff
+      // 0 <= dist < window with dist = (that row + shift - key) = dbase + 32 qb + 8 g4 + e.
+      const int dbase = q0 + 4 * half + shift - key;
+      uint32_t pw[QB][8], dsw[QB][8];
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        // Dropout bytes for (row 32 qb + 8 g4 + 4 half + e, this lane's key), in
+        // register order 4 g4 + e. Lane (c, h) draws row 32 qb + c's bytes for
+        // the 16 keys kw0 + 16 h .. +15 (the forward's Philox contract), stores
+        // them row-major in the wave's tile and reads back its own key column.
+        uint32_t zbyte[16];
+        if constexpr (DROP) {
+          const u32x4 w = philox4x32_10<false>((uint32_t)(kw0 / 16 + half), (uint32_t)(q0 + 32 * qb + col), bhq,
+                                        a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+          lds_write_b128(ztile, col * ZPITCH + 16 * half, w);
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) zbyte[i] = ztile[(8 * (i >> 2) + 4 * half + (i & 3)) * ZPITCH + col];
+        }
+  #pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int rq = qb * 32 + 8 * g4 + 4 * half;
+          const f32x4 l2 = *(const FA_LDS f32x4*)(stt + rq * 4);   // lse2 of rows rq .. rq + 3
+          f32x4 nd{};                                               // their -D, unless folded into dP
+          if constexpr (!FOLD) nd = *(const FA_LDS f32x4*)(stt + C::SLOT + rq * 4);
+          float p[4], ds[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            float pe = exp2_fast(fmaf(s[qb][r], a.c, -l2[e]));
+            if constexpr (decltype(masked)::value) {
+              const int dist = dbase + (qb * 32 + 8 * g4 + e);   // one unsigned compare for the band
+              if (WIN ? (uint32_t)dist >= (uint32_t)a.window : dist < 0) pe = 0.f;
+            }
+            float dpe = dp[qb][r];   // dP - D when folded, else dP
+            float pv = pe;
+            if constexpr (DROP) {   // dV takes the kept P; dP is dropped and rescaled
+              const bool keep = zbyte[r] < a.drop.t;
+              pv = keep ? pe : 0.f;
+              dpe = keep ? dpe * a.drop.inv_keep : 0.f;
+            }
+            if constexpr (!FOLD) dpe += nd[e];
+            p[e] = pv;
+            ds[e] = pe * dpe;
+          }
+          pw[qb][2 * g4] = pack_bf16x2(p[0], p[1]);
+          pw[qb][2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
+          dsw[qb][2 * g4] = pack_bf16x2(ds[0], ds[1]);
+          dsw[qb][2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+        }
+      }
+      // (the hint on the unmasked body only: on the masked one it costs registers)
+      if constexpr (C::IGLP >= 0 && !decltype(masked)::value) __builtin_amdgcn_iglp_opt(C::IGLP);
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const bf16x8 pb = as_bf16x8(u32x4{pw[qb][4 * hs], pw[qb][4 * hs + 1], pw[qb][4 * hs + 2], pw[qb][4 * hs + 3]});
+          const bf16x8 sb = as_bf16x8(u32x4{dsw[qb][4 * hs], dsw[qb][4 * hs + 1], dsw[qb][4 * hs + 2], dsw[qb][4 * hs + 3]});
+          const uint32_t hb = (qb * 32 + hs * 16) * ROWB;
+  #pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const u32x2 glo = lds_read_tr(gt, hb + (tr_lo ^ (64 * db)));
+            const u32x2 ghi = lds_read_tr(gt, hb + (tr_hi ^ (64 * db)));
+            dv_acc[db] = mfma32(as_bf16x8(u32x4{glo[0], glo[1], ghi[0], ghi[1]}), pb, dv_acc[db]);
+            const u32x2 qlo = lds_read_tr(qt, hb + (tr_lo ^ (64 * db)));
+            const u32x2 qhi = lds_read_tr(qt, hb + (tr_hi ^ (64 * db)));
+            dk_acc[db] = mfma32(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dk_acc[db]);
+          }
+        }
+    };
+
+    // Ring of NSTAGE tiles, NSTAGE - 1 loads ahead of the compute. The loop is
+    // unrolled NSTAGE times, so every stage is a compile-time LDS offset.
+    constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::VM_PER_TILE;
+    if (n_iter > 0) {
+      static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(st); });
+      wait_vm_barrier<AHEAD_VM>();          // K/V rows and tile 0 have landed
+    }
+    int cur_qi = DOWN ? n_qt - 1 : qt_begin, cur_h = 0;
+    auto step = [&](auto stage_c, auto may_mask) FA_INLINE {
+      constexpr int CS = decltype(stage_c)::value;
+      issue(std::integral_constant<int, (CS + C::NSTAGE - 1) % C::NSTAGE>{});   // zeros past the end
+      const FA_LDS uint8_t* st = smem + CS * STAGE;
+      const int q0 = cur_qi * BQ;
+      // some (row, key) pair of this wave is masked (causal limit or window start)
+      if (decltype(may_mask)::value &&
+          ((CAUSAL && q0 + shift < kw0 + 31) || (WIN && q0 + BQ - 1 + shift - a.window + 1 > kw0)))
+        body(st, q0, cur_h, std::true_type{});
+      else
+        body(st, q0, cur_h, std::false_type{});
+      wait_vm_barrier<AHEAD_VM>();          // the next tile has landed; this stage is free
+      if constexpr (DOWN) {
+        if (++cur_h == G) {
+          cur_h = 0;
+          --cur_qi;
+        }
+      } else if (++cur_qi == n_qt) {
+        cur_qi = qt_begin;
+        ++cur_h;
+      }
+    };
+    int it = 0;
+    if constexpr (CAUSAL && !WIN) {
+      // tiles whose first row sees every key of the workgroup need no mask; the
+      // downward walk visits them first (whole groups of NSTAGE iterations)
+      const int qi_full = (k0 + C::BK - 1 - shift + BQ - 1) / BQ;   // first tile with no masked pair
+      const int it_full = max(0, n_qt - max(qi_full, qt_begin)) * G / C::NSTAGE * C::NSTAGE;
+      for (; it < it_full; it += C::NSTAGE)
+        static_for<0, C::NSTAGE>([&](auto s) FA_INLINE { step(s, std::false_type{}); });
+    }
+    for (; it < n_iter; it += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto s) FA_INLINE {
+        if (it + decltype(s)::value < n_iter) step(s, std::true_type{});
+      });
+    if (n_iter > 0) wait_vm_barrier<0>();   // no load is left writing LDS when the workgroup exits
+
+    if (key < a.Tk) {
+      uint16_t* dkp = a.dk + kvoff + (size_t)key * D;
+      uint16_t* dvp = a.dv + kvoff + (size_t)key * D;
+  #pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+  #pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * half;
+          const f32x16& kk = dk_acc[db];
+          const f32x16& vv = dv_acc[db];
+          *(u32x2*)(dkp + d0) = u32x2{pack_bf16x2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale),
+                                      pack_bf16x2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale)};
+          const float sv = DROP ? a.drop.inv_keep : 1.f;   // dV = (P Z)^T dO * 256 / t
+          *(u32x2*)(dvp + d0) = u32x2{pack_bf16x2(vv[4 * g4] * sv, vv[4 * g4 + 1] * sv),
+                                      pack_bf16x2(vv[4 * g4 + 2] * sv, vv[4 * g4 + 3] * sv)};
+        }
+    }
+  };
+
+  if constexpr (PAIRK) {
+    key_tile(unit);
+    if (n_ktiles - 1 - unit != unit) {   // the middle tile of an odd count runs alone
+      __syncthreads();                   // every wave is done with the first tile's LDS ring
+      key_tile(n_ktiles - 1 - unit);
+    }
+  } else {
+    key_tile(unit);
   }
 }
 
@@ -805,14 +824,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
   // pair of them), then the query heads that share the kv head, so the
   // workgroups that run together on an XCD read the same K/V tiles at about
   // the same time.
-  //   * Causal without window or dropout, a unit is a pair of query tiles:
+  //   * Causal without a window, a unit is a pair of query tiles:
   //     tile p walks its key tiles up from the first, then tile n - 1 - p
   //     walks its key tiles down from the last. Every workgroup then does the
   //     same number of steps, and after s steps each reads key tile s (first
   //     walk) or (n + 1) BR / BC - 1 - s (second walk) whatever its p (for
   //     Tq = Tk): the resident workgroups share two K/V tiles at a time.
   //   * Otherwise a unit is one query tile, causal ones longest first.
-  constexpr bool PAIR = CAUSAL && !WIN && !DROP;
+  constexpr bool PAIR = CAUSAL && !WIN;
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
   const uint32_t G = (uint32_t)(a.Hq / a.Hkv), per_grp = (uint32_t)n_units * G;
   const uint32_t kvg = t / per_grp, r = t - kvg * per_grp;
@@ -1008,7 +1027,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
       }
       if constexpr (DROP) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j + 1, kb);
+        for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(UP ? j + 1 : j - 1, kb);   // the next tile's
       }
     };
 
@@ -1017,7 +1036,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void bwd_dq_kernel(BwdArgs a, int n_
     constexpr int AHEAD_VM = (C::NSTAGE - 2) * C::DMA_PER_WAVE;
     if constexpr (DROP) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(j_begin, kb);
+      for (int kb = 0; kb < KB; ++kb) zcur[kb] = drop_bytes(tile_of(0), kb);
     }
     if (n_it > 0) {
       static_for<0, C::NSTAGE - 1>([&](auto st) FA_INLINE { issue(decltype(st)::value, st); });
@@ -1116,8 +1135,8 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using QC = typename std::conditional<ALT, DqCfg<D, QD::NW, (QD::BC == 32 ? 64 : 32)>, QD>::type;
   // dq first: it also stores the per-row statistics the dK/dV kernel reads
   const int n_qtiles = (a.Tq + QC::BR - 1) / QC::BR;
-  // causal without window or dropout: one workgroup per pair of query tiles p, n - 1 - p
-  const int n_qunits = CAUSAL && !WIN && !DROP ? (n_qtiles + 1) / 2 : n_qtiles;
+  // causal without a window: one workgroup per pair of query tiles p, n - 1 - p
+  const int n_qunits = CAUSAL && !WIN ? (n_qtiles + 1) / 2 : n_qtiles;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QC, WIN, DROP>), dim3((unsigned)(n_qunits * a.B * a.Hq)), dim3(QC::NT), 0,
                      stream, a, n_qtiles, n_qunits);
   hipError_t e = hipGetLastError();
@@ -1152,7 +1171,9 @@ static hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   } else {
     using KC = typename std::conditional<ALT, DkdvCfg<D, KD::NW, (KD::BQ == 64 ? 32 : 64)>, KD>::type;
     const int n_ktiles = (a.Tk + KC::BK - 1) / KC::BK;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_ktiles * a.B * a.Hkv)), dim3(KC::NT),
+    // causal without a window: one workgroup per pair of key tiles p, n - 1 - p
+    const int n_kunits = CAUSAL && !WIN ? (n_ktiles + 1) / 2 : n_ktiles;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, KC, WIN, DROP>), dim3((unsigned)(n_kunits * a.B * a.Hkv)), dim3(KC::NT),
                        0, stream, a, n_ktiles);
     return hipGetLastError();
   }
