@@ -17,6 +17,7 @@ import numpy as np
 import torch
 
 from io_aware_softmax_05_amd import inputs
+from oracle import attention_ref as ref
 
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
@@ -53,6 +54,48 @@ def check_bf16(name: str, got, ref) -> None:
     refv = np.where(fin, ref, 0.0)
     scaled = float(np.max(np.abs(np.where(fin, got, 0.0) - refv) / np.maximum(1.0, np.abs(refv)), initial=0.0))
     assert scaled <= 2e-2 and rel <= 1e-2, f"{name}: max_abs={max_abs:.3e} (scaled {scaled:.3e}) rel={rel:.3e}"
+
+
+def storage_allowance(hv, scale, causal, dropout=None):
+    """First-order error that bf16 storage of O, P and dS can cause, per
+    output element (unit roundoff u = 2^-8).
+
+    D_i = sum_c dO_ic O_ic is formed from the stored bf16 O, so it may be off
+    by dD_i = u sum_c |dO_ic O_ic|; dS_ij = P_ij (dP_ij - D_i) inherits
+    P_ij dD_i, which matters when a row is dominated by one key (dP_ij and D_i
+    then nearly cancel). P and dS are also rounded to bf16 before their
+    matrix products. With dropout, O and dP carry the keep mask scaled by
+    1 / kappa (the oracle's mask), and O is no longer a copy of a stored V
+    row even where one key holds all the weight, so the cancellation shows
+    up in ordinary causal rows (row 0 sees one key)."""
+    u = 2.0 ** -8
+    q, k, v, do = hv["q"], hv["k"], hv["v"], hv["do"]
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    o, _ = ref.attention_fwd(q, k, v, scale, causal, dropout=dropout)
+    dD = u * np.sum(np.abs(do * o), axis=-1)
+    a_dq, a_dk, a_dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            p, _ = ref.row_probs(q[b, h], k[b, hk], scale, np.arange(Tq), Tq, causal)
+            z = 1.0 if dropout is None else ref.dropout_keep(dropout, b * Hq + h, np.arange(Tq), Tk) / dropout.kappa
+            dp = (do[b, h] @ v[b, hk].T) * z
+            ds = np.abs(p * (dp - (p * dp).sum(axis=1, keepdims=True)))
+            a_dq[b, h] = scale * (dD[b, h][:, None] * (p @ np.abs(k[b, hk])) + u * ds @ np.abs(k[b, hk]))
+            a_dk[b, hk] += scale * (p.T @ (dD[b, h][:, None] * np.abs(q[b, h])) + u * ds.T @ np.abs(q[b, h]))
+            a_dv[b, hk] += u * (p * z).T @ np.abs(do[b, h])
+    return a_dq, a_dk, a_dv
+
+
+def check_with_allowance(name, got, want, allow):
+    """The bf16 rule of check_bf16 with a per-element allowance added to its max-abs term."""
+    got = host(got) if isinstance(got, torch.Tensor) else got
+    _, rel = report(name, got, want)
+    excess = np.abs(got - want) - (2e-2 * np.maximum(1.0, np.abs(want)) + allow)
+    print(f"    worst excess over allowance {float(excess.max()):.3e}", flush=True)
+    assert float(excess.max()) <= 0.0 and rel <= 1e-2, name
 
 
 def check_f32(name: str, got, ref) -> None:

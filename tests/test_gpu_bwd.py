@@ -89,43 +89,6 @@ def test_bwd_random_shapes(shape):
     gu.check_bf16("dV", dv, dv_r)
 
 
-def _storage_allowance(hv, scale, causal):
-    """First-order error that bf16 storage of O, P and dS can cause, per
-    output element (unit roundoff u = 2^-8).
-
-    D_i = sum_c dO_ic O_ic is formed from the stored bf16 O, so it may be off
-    by dD_i = u sum_c |dO_ic O_ic|; dS_ij = P_ij (dP_ij - D_i) inherits
-    P_ij dD_i, which matters when a row is dominated by one key (dP_ij and D_i
-    then nearly cancel). P and dS are also rounded to bf16 before their
-    matrix products."""
-    u = 2.0 ** -8
-    q, k, v, do = hv["q"], hv["k"], hv["v"], hv["do"]
-    B, Hq, Tq, d = q.shape
-    Hkv, Tk = k.shape[1], k.shape[2]
-    g = Hq // Hkv
-    o, _ = ref.attention_fwd(q, k, v, scale, causal)
-    dD = u * np.sum(np.abs(do * o), axis=-1)
-    a_dq, a_dk, a_dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    for b in range(B):
-        for h in range(Hq):
-            hk = h // g
-            p, _ = ref.row_probs(q[b, h], k[b, hk], scale, np.arange(Tq), Tq, causal)
-            dp = do[b, h] @ v[b, hk].T
-            ds = np.abs(p * (dp - (p * dp).sum(axis=1, keepdims=True)))
-            a_dq[b, h] = scale * (dD[b, h][:, None] * (p @ np.abs(k[b, hk])) + u * ds @ np.abs(k[b, hk]))
-            a_dk[b, hk] += scale * (p.T @ (dD[b, h][:, None] * np.abs(q[b, h])) + u * ds.T @ np.abs(q[b, h]))
-            a_dv[b, hk] += u * p.T @ np.abs(do[b, h])
-    return a_dq, a_dk, a_dv
-
-
-def _check_with_allowance(name, got, want, allow):
-    got = gu.host(got)
-    _, rel = gu.report(name, got, want)
-    excess = np.abs(got - want) - (2e-2 * np.maximum(1.0, np.abs(want)) + allow)
-    print(f"    worst excess over allowance {float(excess.max()):.3e}", flush=True)
-    assert float(excess.max()) <= 0.0 and rel <= 1e-2, name
-
-
 @pytest.mark.parametrize("gain", [4.0, 8.0])
 def test_bwd_peaky_scores(gain):
     """Queries scaled up so scores have sigma ~ gain: rows are dominated by a
@@ -135,10 +98,10 @@ def test_bwd_peaky_scores(gain):
     hv, dev = gu.attention_case(17, 1, 4, 2, 200, 200, 128, with_dout=True, q_gain=gain)
     dq, dk, dv = _fwd_bwd(dev, True, scale)
     dq_r, dk_r, dv_r = ref.attention_bwd(hv["q"], hv["k"], hv["v"], hv["do"], scale, True)
-    a_dq, a_dk, a_dv = _storage_allowance(hv, scale, True)
-    _check_with_allowance("dQ", dq, dq_r, a_dq)
-    _check_with_allowance("dK", dk, dk_r, a_dk)
-    _check_with_allowance("dV", dv, dv_r, a_dv)
+    a_dq, a_dk, a_dv = gu.storage_allowance(hv, scale, True)
+    gu.check_with_allowance("dQ", dq, dq_r, a_dq)
+    gu.check_with_allowance("dK", dk, dk_r, a_dk)
+    gu.check_with_allowance("dV", dv, dv_r, a_dv)
 
 
 def test_bwd_deterministic():
