@@ -159,9 +159,9 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
-  // one wave per query row, a few rows per workgroup
+  // one wave per query row, a few rows of one head per workgroup
   const int rows_per_group = fa::fwd_f32_rows_per_workgroup();
-  if (((int64_t)B * Hq * Tq + rows_per_group - 1) / rows_per_group > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * Hq * ((Tq + rows_per_group - 1) / rows_per_group) > INT32_MAX) return FA_ERR_INVALID_ARG;
   fa::FwdF32Args a{};
   a.q = static_cast<const float*>(q);
   a.k = static_cast<const float*>(k);
