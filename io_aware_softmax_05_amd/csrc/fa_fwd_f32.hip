@@ -9,13 +9,13 @@
 //
 // Layout: one wave per query row, four rows of one head per workgroup, so
 // even a single head of 256 rows spreads over 64 workgroups. The keys stream
-// past the rows in tiles of 64: the workgroup copies a tile's K and V rows
-// into LDS once (coalesced 16-byte loads, the next tile's loads issued before
-// the current tile is scored), lane l scores key t0 + l with the whole query
-// row in its registers, the tile's maximum and sum are wave reductions, and
-// for u += p V each lane owns D / 64 output columns, taking every key's
-// probability from the lane that scored it (a readlane) and the value from
-// the tile in LDS. m and l are the same in every lane of the wave; u is
+// past the rows in tiles of 64 KPL: the workgroup copies a tile's K and V
+// rows into LDS once (coalesced 16-byte loads, the next tile's loads issued
+// before the current tile is scored), lane l scores keys t0 + 64 r + l
+// (r < KPL) with the whole query row in its registers, the tile's maximum
+// and sum are wave reductions, and for u += p V each lane owns D / 64 output
+// columns, taking every key's probability from the lane that scored it (a
+// readlane) and the value from the tile in LDS. m and l are the same in every lane of the wave; u is
 // spread over the lanes. l is a compensated sum, so long rows keep fp32
 // accuracy.
 #include "fa_common.hpp"
@@ -26,7 +26,10 @@ namespace fa {
 namespace {
 
 constexpr int kF32RowsPerGroup = 4;   // waves (query rows of one head) per workgroup
-constexpr int kF32TileKeys = 64;      // keys per tile: one per lane
+// keys per lane per tile: 2 at d = 64 (128-key tiles), 1 at d = 128, whose
+// 128-key tiles would need 132 KB of LDS and hold one workgroup per CU
+template <int D>
+constexpr int kF32KeysPerLane = D == 64 ? 2 : 1;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -43,7 +46,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kF32RowsPerGroup) void fwd_f32_kernel(FwdF32Args a) {
-  constexpr int NW = kF32RowsPerGroup, TK = kF32TileKeys, CPL = D / 64;   // output columns per lane
+  constexpr int NW = kF32RowsPerGroup, KPL = kF32KeysPerLane<D>, TK = 64 * KPL;
+  constexpr int CPL = D / 64;                    // output columns per lane
   constexpr int CH = D / 4;                      // 16-byte chunks per row
   constexpr int KP = D + 4;                      // K row pitch in LDS (floats): the 16 lanes of a
                                                  // 128-bit row read land on distinct banks
@@ -112,49 +116,67 @@ __global__ __launch_bounds__(64 * kF32RowsPerGroup) void fwd_f32_kernel(FwdF32Ar
     if (t0 + TK < wg_end) load(t0 + TK);   // in flight while this tile is used
     if (!live || t0 >= kv_end) continue;    // wave-uniform: no key of the tile is visible to the row
 
-    // S for this lane's key of the tile (masked keys: -inf)
-    const int key = t0 + lane;
-    float s = -INFINITY;
-    if (key < kv_end) {
-      const float4* kr = (const float4*)&ks[lane * KP];
-      float acc = 0.f;
+    // S for this lane's keys of the tile (masked keys: -inf)
+    float sk[KPL];
+    float mt = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const float4 kv = kr[c];
-        acc = fmaf(q[4 * c], kv.x, acc);
-        acc = fmaf(q[4 * c + 1], kv.y, acc);
-        acc = fmaf(q[4 * c + 2], kv.z, acc);
-        acc = fmaf(q[4 * c + 3], kv.w, acc);
+    for (int r = 0; r < KPL; ++r) {
+      const int key = t0 + 64 * r + lane;
+      float sv = -INFINITY;
+      if (key < kv_end) {
+        const float4* kr = (const float4*)&ks[(64 * r + lane) * KP];
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const float4 kv = kr[c];
+          acc = fmaf(q[4 * c], kv.x, acc);
+          acc = fmaf(q[4 * c + 1], kv.y, acc);
+          acc = fmaf(q[4 * c + 2], kv.z, acc);
+          acc = fmaf(q[4 * c + 3], kv.w, acc);
+        }
+        sv = acc * a.scale;
       }
-      s = acc * a.scale;
+      sk[r] = sv;
+      mt = fmaxf(mt, sv);
     }
     // m' = max(m, tile max); l and u are rescaled together by e^(m - m')
-    const float m_new = fmaxf(m, wave_max(s));   // finite: key t0 is visible
+    const float m_new = fmaxf(m, wave_max(mt));   // finite: key t0 is visible
     const float alpha = expf(m - m_new);         // 0 while m is still -inf
     l *= alpha;
     lc *= alpha;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) u[e] *= alpha;
     m = m_new;
-    const float p = expf(s - m);                 // exactly 0 for a masked key
-    kahan_add(l, lc, wave_sum(p));
-    // u += sum_j p_j V_j over the tile's visible keys
+    float pk[KPL], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      pk[r] = expf(sk[r] - m);   // exactly 0 for a masked key
+      psum += pk[r];
+    }
+    kahan_add(l, lc, wave_sum(psum));
+    // u += sum_j p_j V_j over the tile's visible keys, 64 keys per block
     const float* vr = vs + CPL * lane;
-    auto add_key = [&](int j) {
-      const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j));
+    auto add_key = [&](int r, int j) {
+      const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pk[r]), j));
+      const int row = 64 * r + j;
       if constexpr (CPL == 1) {
-        u[0] = fmaf(pj, vr[j * D], u[0]);
+        u[0] = fmaf(pj, vr[row * D], u[0]);
       } else {
-        const float2 v2 = *(const float2*)(vr + j * D);
+        const float2 v2 = *(const float2*)(vr + row * D);
         u[0] = fmaf(pj, v2.x, u[0]);
         u[1] = fmaf(pj, v2.y, u[1]);
       }
     };
-    if (kv_end - t0 >= TK) {
 #pragma unroll
-      for (int j = 0; j < TK; ++j) add_key(j);
-    } else {   // the row's last, partial tile: only its visible keys
-      for (int j = 0; j < kv_end - t0; ++j) add_key(j);
+    for (int r = 0; r < KPL; ++r) {
+      const int n = kv_end - t0 - 64 * r;
+      if (n <= 0) break;
+      if (n >= 64) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) add_key(r, j);
+      } else {   // the row's last, partial block: only its visible keys
+        for (int j = 0; j < n; ++j) add_key(r, j);
+      }
     }
   }
 
